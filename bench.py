@@ -1,0 +1,260 @@
+"""Benchmark: top-k block-sparse attention on the 720p Wan2.1-14B-shaped workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--config 3] [--topk 0.3]
+
+One step is the whole path on one batch of resident inputs: block pooling of
+Q and K, pooled scoring with per-row top-k selection, and block-sparse
+attention (sparge_attn_topk). Prints ONE JSON line on stdout; progress goes to
+stderr. Alongside the step it reports:
+  - the attention kernel alone (sparge_attn_from_list over the predicted
+    lists), timed launch by launch with HIP events on the stream it runs on,
+    as effective and dense-equivalent TFLOP/s against the bf16 MFMA peak;
+  - pooling (GB/s) and prediction (GFLOP/s, GB/s) kernels;
+  - block_sparse_attn with the predicted mask as a user mask (compaction + attention);
+  - the fp64 CPU oracle timed on the host cores on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 4096 flop/clk x 2.4 GHz (MI355X dense bf16 MFMA)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector
+METRIC = "block-sparse attn TFLOPS (effective + dense-equiv) & ms/call, N=75600 topk=0.3"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_wan14b-720p_topk0.3_traffic.json")
+ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_sparge_amd", "csrc", "attn_fwd.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", type=int, default=3)
+    p.add_argument("--topk", type=float, default=None)
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def effective_flops(mask: np.ndarray, N: int, D: int) -> float:
+    """4*D * sum over kept tiles of (valid query rows) x (valid keys)."""
+    qb, kb = mask.shape[-2:]
+    rows = np.full(qb, 128.0)
+    rows[-1] = N - 128 * (qb - 1)
+    cols = np.full(kb, 64.0)
+    cols[-1] = N - 64 * (kb - 1)
+    per_row = mask.reshape(-1, qb, kb).astype(np.float64) @ cols        # (BH, qb)
+    return 4.0 * D * float((per_row @ rows).sum())
+
+
+def kernel_durations_ms(fn, iters):
+    """Per-launch durations from HIP events recorded on the current stream around each launch."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(per_launch_flops):
+    """HBM bytes per attention launch from the committed rocprofv3 counter runs, if still current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("attn_fwd_source_sha256_16") != source_hash(ATTN_SOURCE):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, q, k, v, topk, budget_s):
+    """The fp64 oracle on the host cores: head 0's full prediction plus attention for as
+    many of its query blocks as fit in the time budget (in block order)."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except ImportError:                                          # pragma: no cover
+        threadpool_limits, threadpool_info = None, None
+    cores = len(os.sched_getaffinity(0))
+    ctx = threadpool_limits(cores) if threadpool_limits else None
+    try:
+        if ctx:
+            ctx.__enter__()
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1]) if threadpool_info else 1
+        f64 = synth.bf16_bits_to_f64
+        qh, kh, vh = f64(q[0, 0]), f64(k[0, 0]), f64(v[0, 0])
+        t0 = time.perf_counter()
+        pr = oracle.predict_mask(qh[None, None], kh[None, None], topk)
+        t_pred = time.perf_counter() - t0
+        m = pr["mask"][0, 0]
+        qb = m.shape[0]
+        done, t_attn, flops = 0, 0.0, 0.0
+        N, D = qh.shape
+        while done < qb and (done < 4 or t_pred + t_attn < budget_s):
+            rows = np.arange(128 * done, min(N, 128 * done + 128))
+            t1 = time.perf_counter()
+            oracle.masked_attention_rows(qh, kh, vh, m, rows)
+            t_attn += time.perf_counter() - t1
+            flops += effective_flops(m[done:done + 1][None], N, D) if done < qb - 1 else \
+                effective_flops(m[None, -1:], N, D) * (len(rows) / 128.0)
+            done += 1
+        bh = wl.B * wl.H
+        full_attn_s = t_attn * (qb / done) * bh
+        full_pred_s = t_pred * bh
+        return {
+            "value": flops / t_attn / 1e12,
+            "unit": "TFLOPS",
+            "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"head 0 of {bh}: full prediction ({t_pred:.2f} s) and masked attention of "
+                       f"query blocks 0..{done - 1} of {qb} ({t_attn:.2f} s, {flops / 1e9:.1f} GFLOP); "
+                       f"value = sampled attention flops / time"),
+            "extrapolated_full_step_s": full_attn_s + full_pred_s,
+            "host_cpus": cores,
+        }
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the path shards by (batch, head) with no "
+              "exchange, and multi-GPU runs are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import block_sparse_attention_sparge_amd as sp
+    import synth
+
+    wl = synth.WORKLOADS[args.config]
+    topk = args.topk if args.topk is not None else (0.3 if args.config == 3 else wl.topks[0])
+    B, H, N, D = wl.B, wl.H, wl.N, wl.D
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sp.load_library()
+
+    log(f"generating {wl.describe()} seed={args.seed}")
+    q, k, v = synth.make_qkv(wl, seed=args.seed)
+    tod = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    dq, dk, dv = tod(q), tod(k), tod(v)
+    out = torch.empty_like(dq)
+    mask = torch.empty(sp.mask_shape(B, H, N), dtype=torch.uint8, device=dev)
+    ws = torch.empty(sp.workspace_bytes(B, H, N, D, topk), dtype=torch.uint8, device=dev)
+    kk = sp.topk_count(mask.shape[-1], topk)
+
+    def step():
+        sp.attn_topk(dq, dk, dv, topk=topk, out=out, workspace=ws)
+
+    # mask and lists once, for the per-kernel timings and the flop count
+    sp.attn_topk(dq, dk, dv, topk=topk, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    qbar, kbar = sp.pool_blocks(dq, 128), sp.pool_blocks(dk, 64)
+    mask_t, idx, cnt = sp.predict_mask(qbar, kbar, N, topk)
+    torch.cuda.synchronize()
+    m = mask_t.cpu().numpy()
+    eff = effective_flops(m, N, D)
+    dense = 4.0 * B * H * N * N * D
+    log(f"k={kk} of {m.shape[-1]} key blocks; effective {eff / 1e12:.2f} TFLOP, dense {dense / 1e12:.2f} TFLOP")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done; timing {args.steps} steps")
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    log(f"step {ms:.3f} ms")
+
+    # attention kernel alone, launch by launch
+    attn_iters = max(5, min(args.steps, 20))
+    attn = kernel_durations_ms(lambda: sp.attn_from_list(dq, dk, dv, idx, cnt, out=out), attn_iters)
+    attn_ms = float(np.mean(attn))
+    log(f"attention kernel {attn_ms:.3f} ms (min {min(attn):.3f})")
+    pool_q = kernel_durations_ms(lambda: sp.pool_blocks(dq, 128), 10)
+    pool_k = kernel_durations_ms(lambda: sp.pool_blocks(dk, 64), 10)
+    pred = kernel_durations_ms(lambda: sp.predict_mask(qbar, kbar, N, topk, return_mask=True), 10)
+    bsa = kernel_durations_ms(lambda: sp.block_sparse_attn(dq, dk, dv, mask_id=mask_t, out=out), 5)
+
+    qb_, kb_ = m.shape[-2:]
+    pool_bytes_q = B * H * N * D * 2 + B * H * qb_ * D * 4
+    pool_bytes_k = B * H * N * D * 2 + B * H * kb_ * D * 4
+    pred_flops = 2.0 * B * H * qb_ * kb_ * D
+    pred_bytes = B * H * (qb_ + kb_) * D * 4 + B * H * qb_ * (kb_ + 4 * kk + 4)
+    achieved = eff / (attn_ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": eff / (ms * 1e-3) / 1e12,
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "H": H, "N": N, "D": D, "topk": topk, "k": kk,
+                   "n_qblocks": int(qb_), "n_kblocks": int(kb_), "seed": args.seed,
+                   "step": "sparge_attn_topk (pool Q, pool K, predict, attention)"},
+        "dense_equiv_tflops": dense / (ms * 1e-3) / 1e12,
+        "frac_peak_effective": eff / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "frac_peak_dense_equiv": dense / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "effective_tflop_per_step": eff / 1e12,
+        "attention_kernel": {"ms": attn_ms, "ms_min": float(min(attn)),
+                             "effective_tflops": achieved,
+                             "dense_equiv_tflops": dense / (attn_ms * 1e-3) / 1e12},
+        "block_sparse_attn_ms": float(np.mean(bsa)),
+        "pool_q": {"ms": float(np.mean(pool_q)), "gbs": pool_bytes_q / (np.mean(pool_q) * 1e-3) / 1e9},
+        "pool_k": {"ms": float(np.mean(pool_k)), "gbs": pool_bytes_k / (np.mean(pool_k) * 1e-3) / 1e9},
+        "predict": {"ms": float(np.mean(pred)),
+                    "gflops_fp32": pred_flops / (np.mean(pred) * 1e-3) / 1e9,
+                    "gbs": pred_bytes / (np.mean(pred) * 1e-3) / 1e9},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": load_traffic(eff),
+                     "kernel": "attn_fwd_kernel<128> (sparge_attn_from_list)"},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle sample")
+        result["cpu_baseline"] = cpu_baseline(wl, q, k, v, topk, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,46 @@
+// Internal declarations shared by the host API and the gfx950 kernels of libsparge.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sparge {
+
+constexpr int kQBlock = 128;   // query rows per block
+constexpr int kKBlock = 64;    // key rows per block
+constexpr int kNumXcd = 8;     // MI355X: 8 accelerator complex dies, each with its own L2
+
+// Shape of one (B, H, N, D) bf16 operand: element strides of the B, H, N axes.
+struct Strides {
+  int64_t b, h, n;
+};
+
+// Launchers. Each validates nothing (the C API has done it) and returns the
+// launch status of its kernel(s).
+hipError_t launch_pool(const uint16_t* x, int64_t B, int64_t H, int64_t N, int D, Strides s,
+                       int block_rows, float* out, hipStream_t stream);
+
+hipError_t launch_predict(const float* qbar, const float* kbar, int64_t BH, int64_t N, int D,
+                          int64_t k, float scale, uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt,
+                          hipStream_t stream);
+
+hipError_t launch_compact(const uint8_t* mask, int64_t rows, int64_t n_kb, int32_t* kv_idx,
+                          int32_t* kv_cnt, hipStream_t stream);
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  const int32_t* kv_idx;   // nullptr: dense
+  const int32_t* kv_cnt;
+  int64_t ld_idx;
+  int64_t B, H, N;
+  int D;
+  Strides qs, ks, vs, os;
+  float scale;
+};
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace sparge

@@ -1,0 +1,46 @@
+// Mask compaction: mask_id rows (uint8, nonzero = kept) -> ascending kept-block lists.
+//
+// Turns a user block mask (SpargeAttention Documentation, block_sparse_sage2_attn_cuda
+// and "Mask Requirements") into the per-query-block list the attention kernel
+// walks, so that masked tiles are never loaded. One wavefront per mask row:
+// 64 bytes per step, a ballot and a prefix count place each kept id.
+#include "common.h"
+
+namespace sparge {
+namespace {
+
+__device__ __forceinline__ uint32_t count_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+}
+
+__global__ __launch_bounds__(256) void compact_kernel(const uint8_t* __restrict__ mask,
+                                                      int64_t rows, int64_t n_kb,
+                                                      int32_t* __restrict__ kv_idx,
+                                                      int32_t* __restrict__ kv_cnt) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const uint8_t* m = mask + row * n_kb;
+  int32_t* out = kv_idx + row * n_kb;
+  int64_t base = 0;
+  for (int64_t j0 = 0; j0 < n_kb; j0 += 64) {
+    const int64_t j = j0 + lane;
+    const bool sel = (j < n_kb) && m[j] != 0;
+    const uint64_t b = __ballot(sel);
+    if (sel) out[base + count_below(b)] = static_cast<int32_t>(j);
+    base += __popcll(b);
+  }
+  if (lane == 0) kv_cnt[row] = static_cast<int32_t>(base);
+}
+
+}  // namespace
+
+hipError_t launch_compact(const uint8_t* mask, int64_t rows, int64_t n_kb, int32_t* kv_idx,
+                          int32_t* kv_cnt, hipStream_t stream) {
+  void* args[] = {(void*)&mask, (void*)&rows, (void*)&n_kb, (void*)&kv_idx, (void*)&kv_cnt};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&compact_kernel),
+                         dim3(static_cast<uint32_t>((rows + 3) / 4)), dim3(256), args, 0, stream);
+}
+
+}  // namespace sparge

@@ -1,0 +1,200 @@
+// Pooled-block scoring and per-row top-k selection.
+//
+// For every query block i of a head: s[i][j] = scale * qbar_i . kbar_j over the
+// head's key blocks j (fp32 FMAs), then keep the k largest s, ties going to the
+// lower j. Ranking s ranks the row's softmax identically (softmax is strictly
+// increasing within a row), so no exponentials are needed. Outputs the 0/1
+// mask row (mask_id of SpargeAttention Documentation, "Mask Requirements") and
+// the ascending list of kept key blocks that the attention kernel walks.
+//
+// One workgroup (4 wavefronts) takes R query blocks of one head. Scores for
+// all R rows live in LDS. Selection is an exact radix select on order-preserving
+// 32-bit keys (4 passes of 8 bits, LDS histograms, wavefront prefix sums), one
+// wavefront per row; the final pass emits the list in index order with ballots.
+// No atomics touch global memory, so repeated runs give identical bytes.
+#include "common.h"
+
+namespace sparge {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+// Float -> uint32 whose unsigned order matches the float order (-0 folded to +0).
+__device__ __forceinline__ uint32_t order_key(float s) {
+  const uint32_t u = __float_as_uint(s + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Number of set bits of `m` in lanes below this lane.
+__device__ __forceinline__ uint32_t count_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+}
+
+template <int D, int R>
+__global__ __launch_bounds__(kThreads) void predict_kernel(
+    const float* __restrict__ qbar, const float* __restrict__ kbar, int64_t n_qb, int64_t n_kb,
+    int64_t n_groups, int64_t k, float scale, uint8_t* __restrict__ mask,
+    int32_t* __restrict__ kv_idx, int32_t* __restrict__ kv_cnt) {
+  extern __shared__ float4 smem4[];
+  float* q_lds = reinterpret_cast<float*>(smem4);          // [R][D]
+  float* sc = q_lds + R * D;                               // [R][n_kb]
+  uint32_t* hist = reinterpret_cast<uint32_t*>(sc + R * n_kb);   // [kWaves][256]
+
+  const int64_t bh = blockIdx.x / n_groups;
+  const int64_t row0 = (blockIdx.x - bh * n_groups) * R;   // first query block of this group
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+
+  // Stage the R pooled query rows (zeros past the last query block).
+  for (int e = t; e < R * D; e += kThreads) {
+    const int r = e / D;
+    const int64_t qi = row0 + r;
+    q_lds[e] = (qi < n_qb) ? qbar[(bh * n_qb + qi) * D + (e - r * D)] : 0.f;
+  }
+  __syncthreads();
+
+  // Scores: thread t takes key blocks t, t+256, ... and all R rows.
+  const float* kb_head = kbar + bh * n_kb * D;
+  for (int64_t j = t; j < n_kb; j += kThreads) {
+    const float4* kr = reinterpret_cast<const float4*>(kb_head + j * D);
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+#pragma unroll 4
+    for (int d4 = 0; d4 < D / 4; ++d4) {
+      const float4 kv = kr[d4];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float4 qv = reinterpret_cast<const float4*>(q_lds + r * D)[d4];
+        acc[r] = fmaf(qv.x, kv.x, acc[r]);
+        acc[r] = fmaf(qv.y, kv.y, acc[r]);
+        acc[r] = fmaf(qv.z, kv.z, acc[r]);
+        acc[r] = fmaf(qv.w, kv.w, acc[r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) sc[r * n_kb + j] = scale * acc[r];
+  }
+  __syncthreads();
+
+  // Selection: wavefront `wave` takes rows wave, wave + 4, ...; every wavefront
+  // runs the same number of rounds so the block-wide barriers stay uniform.
+  uint32_t* h = hist + wave * 256;
+  constexpr int kRounds = (R + kWaves - 1) / kWaves;
+  for (int round = 0; round < kRounds; ++round) {
+    const int r = wave + round * kWaves;
+    const int64_t qi = row0 + r;
+    const bool active = (r < R) && (qi < n_qb);
+    const float* srow = sc + (r < R ? r : 0) * n_kb;
+
+    uint32_t prefix = 0, prefix_mask = 0;
+    int64_t kk = k;   // how many still to take among keys matching the prefix
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) h[lane * 4 + q] = 0u;
+      __syncthreads();
+      if (active) {
+        for (int64_t j = lane; j < n_kb; j += 64) {
+          const uint32_t u = order_key(srow[j]);
+          if ((u & prefix_mask) == prefix) atomicAdd(&h[(u >> shift) & 255u], 1u);
+        }
+      }
+      __syncthreads();
+      // Lane L owns bins 4L..4L+3. above(d) = number of candidates with a larger digit.
+      const uint32_t c0 = h[lane * 4 + 0], c1 = h[lane * 4 + 1], c2 = h[lane * 4 + 2],
+                     c3 = h[lane * 4 + 3];
+      const uint32_t mine = c0 + c1 + c2 + c3;
+      // inclusive suffix sum over lanes (lanes above contribute larger digits)
+      uint32_t suf = mine;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_down(suf, off, 64);
+        if (lane + off < 64) suf += o;
+      }
+      const int64_t above3 = static_cast<int64_t>(suf - mine);
+      const int64_t above2 = above3 + c3, above1 = above2 + c2, above0 = above1 + c1;
+      int digit = -1;
+      int64_t above = 0;
+      if (above3 < kk && kk <= above3 + c3) { digit = lane * 4 + 3; above = above3; }
+      else if (above2 < kk && kk <= above2 + c2) { digit = lane * 4 + 2; above = above2; }
+      else if (above1 < kk && kk <= above1 + c1) { digit = lane * 4 + 1; above = above1; }
+      else if (above0 < kk && kk <= above0 + c0) { digit = lane * 4 + 0; above = above0; }
+      const uint64_t who = __ballot(digit >= 0);
+      const int src = who ? (__builtin_ctzll(who)) : 0;
+      digit = __shfl(digit, src, 64);
+      const int64_t above_sel = __shfl(above, src, 64);
+      prefix |= static_cast<uint32_t>(digit < 0 ? 0 : digit) << shift;
+      prefix_mask |= 255u << shift;
+      kk -= above_sel;
+    }
+    // prefix is now the k-th largest key; take every larger key and the first
+    // kk keys equal to it in index order.
+    if (active) {
+      const uint32_t thr = prefix;
+      const int64_t row = bh * n_qb + qi;
+      int32_t* out_idx = kv_idx + row * k;
+      uint8_t* out_mask = mask ? mask + row * n_kb : nullptr;
+      int64_t base = 0, eq_seen = 0;
+      for (int64_t j0 = 0; j0 < n_kb; j0 += 64) {
+        const int64_t j = j0 + lane;
+        const bool valid = j < n_kb;
+        const uint32_t u = valid ? order_key(srow[j]) : 0u;
+        const bool is_eq = valid && u == thr;
+        const uint64_t eq_b = __ballot(is_eq);
+        const int64_t eq_rank = eq_seen + count_below(eq_b);
+        const bool sel = valid && (u > thr || (is_eq && eq_rank < kk));
+        const uint64_t sel_b = __ballot(sel);
+        const int64_t pos = base + count_below(sel_b);
+        if (sel && pos < k) out_idx[pos] = static_cast<int32_t>(j);
+        if (out_mask && valid) out_mask[j] = sel ? 1 : 0;
+        base += __popcll(sel_b);
+        eq_seen += __popcll(eq_b);
+      }
+      if (lane == 0) kv_cnt[row] = static_cast<int32_t>(k);
+    }
+  }
+}
+
+template <int D, int R>
+hipError_t launch_predict_t(const float* qbar, const float* kbar, int64_t BH, int64_t n_qb,
+                            int64_t n_kb, int64_t k, float scale, uint8_t* mask, int32_t* kv_idx,
+                            int32_t* kv_cnt, hipStream_t stream) {
+  const int64_t n_groups = (n_qb + R - 1) / R;
+  const size_t lds = sizeof(float) * (R * D + R * n_kb) + sizeof(uint32_t) * kWaves * 256;
+  void* args[] = {(void*)&qbar, (void*)&kbar, (void*)&n_qb, (void*)&n_kb, (void*)&n_groups,
+                  (void*)&k, (void*)&scale, (void*)&mask, (void*)&kv_idx, (void*)&kv_cnt};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&predict_kernel<D, R>),
+                         dim3(static_cast<uint32_t>(BH * n_groups)), dim3(kThreads), args, lds,
+                         stream);
+}
+
+template <int D>
+hipError_t launch_predict_d(const float* qbar, const float* kbar, int64_t BH, int64_t n_qb,
+                            int64_t n_kb, int64_t k, float scale, uint8_t* mask, int32_t* kv_idx,
+                            int32_t* kv_cnt, hipStream_t stream) {
+  if (n_kb <= 1536)
+    return launch_predict_t<D, 8>(qbar, kbar, BH, n_qb, n_kb, k, scale, mask, kv_idx, kv_cnt, stream);
+  if (n_kb <= 3072)
+    return launch_predict_t<D, 4>(qbar, kbar, BH, n_qb, n_kb, k, scale, mask, kv_idx, kv_cnt, stream);
+  if (n_kb <= 6144)
+    return launch_predict_t<D, 2>(qbar, kbar, BH, n_qb, n_kb, k, scale, mask, kv_idx, kv_cnt, stream);
+  return launch_predict_t<D, 1>(qbar, kbar, BH, n_qb, n_kb, k, scale, mask, kv_idx, kv_cnt, stream);
+}
+
+}  // namespace
+
+hipError_t launch_predict(const float* qbar, const float* kbar, int64_t BH, int64_t N, int D,
+                          int64_t k, float scale, uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt,
+                          hipStream_t stream) {
+  const int64_t n_qb = (N + kQBlock - 1) / kQBlock;
+  const int64_t n_kb = (N + kKBlock - 1) / kKBlock;
+  if (D == 128)
+    return launch_predict_d<128>(qbar, kbar, BH, n_qb, n_kb, k, scale, mask, kv_idx, kv_cnt, stream);
+  return launch_predict_d<64>(qbar, kbar, BH, n_qb, n_kb, k, scale, mask, kv_idx, kv_cnt, stream);
+}
+
+}  // namespace sparge

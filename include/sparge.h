@@ -1,0 +1,173 @@
+/*
+ * sparge.h - C ABI of libsparge, block-sparse self-attention for AMD MI355X (gfx950).
+ *
+ * The method (SpargeAttention Documentation, the recommended top-k API and
+ * "Mask Requirements"; Apply SpargeAttn, opening section) has two parts:
+ *
+ *   1. Mask prediction. Q is mean-pooled over 128-row blocks and K over 64-row
+ *      blocks; pooled blocks are scored with softmax(qbar . kbar^T * scale)
+ *      over the key blocks of each query block; each query block keeps the
+ *      ceil(topk * n_kblocks) best key blocks, ties going to the lower key-block
+ *      index. The result is mask_id of shape (B, H, ceil(N/128), ceil(N/64))
+ *      with 0/1 entries.
+ *   2. Attention. Non-causal softmax attention in which query block i only sees
+ *      the keys of the key blocks its mask row selects. Skipped 128x64 tiles
+ *      are never read.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Q, K, V and O are bf16, passed as uint16_t bit patterns, with logical
+ *    shape (B, H, N, D) as in torch's scaled_dot_product_attention (the
+ *    top-k API is a drop-in for it). Their element strides for the B, H and N
+ *    axes are passed as int64_t[3]; the D axis must be contiguous. Every
+ *    stride must be a non-negative multiple of 8 elements and every base
+ *    address 16-byte aligned, so that a row of 8 bf16 is one aligned load.
+ *  - D (head dimension) must be 64 or 128. N >= 1, B >= 1, H >= 1.
+ *  - N_QB = ceil(N/128) query blocks and N_KB = ceil(N/64) key blocks.
+ *  - scale <= 0 means the default 1/sqrt(D).
+ *  - Pointers are device pointers unless a parameter says otherwise. The
+ *    caller owns every buffer. The library allocates no memory and keeps no
+ *    state between calls.
+ *  - stream is a hipStream_t passed as void* (NULL = the default stream).
+ *    Every call only enqueues work on it and returns without synchronising.
+ *  - All arguments are validated on the host before any HIP call is made, so
+ *    a rejected call has no side effect. Calls return SPARGE_OK (0) or one of
+ *    the negative status codes below; no C++ exception crosses the ABI.
+ *  - Calls that race on the same output buffers on different streams are the
+ *    caller's responsibility; the library itself uses no global memory other
+ *    than the buffers it is given and no atomics on them.
+ */
+#ifndef SPARGE_H
+#define SPARGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPARGE_OK 0
+#define SPARGE_ERR_NULL -1       /* a required pointer is NULL */
+#define SPARGE_ERR_SHAPE -2      /* B, H or N < 1, D not 64/128, N beyond the supported maximum */
+#define SPARGE_ERR_TOPK -3       /* topk not in (0, 1] (or NaN) */
+#define SPARGE_ERR_STRIDE -4     /* negative / unaligned stride or pointer, or an output layout that overlaps itself */
+#define SPARGE_ERR_ALIAS -5      /* an output range overlaps an input range */
+#define SPARGE_ERR_WORKSPACE -6  /* workspace NULL or smaller than sparge_workspace_bytes() */
+#define SPARGE_ERR_ARG -7        /* another invalid argument (e.g. block_rows not 64/128) */
+#define SPARGE_ERR_LAUNCH -8     /* the HIP runtime rejected a kernel launch */
+
+/* Query rows per query block and key rows per key block
+ * (SpargeAttention Documentation, "Mask Requirements": fixed 128x64 blocks). */
+#define SPARGE_Q_BLOCK 128
+#define SPARGE_K_BLOCK 64
+
+/* Largest sequence length the mask-prediction calls accept (one row of
+ * N_KB fp32 scores must fit in on-chip LDS). Attention alone has no such limit. */
+#define SPARGE_MAX_PREDICT_N 786432
+
+/* Static description of a status code (never NULL). */
+const char *sparge_status_string(int status);
+
+/* Host-only helper: the number of key blocks each query block keeps,
+ * k = ceil(topk * n_kblocks) evaluated in IEEE double, where a product within
+ * 1e-9 of an integer counts as that integer; clamped to [1, n_kblocks].
+ * Writes k to *k_out. Errors: SPARGE_ERR_NULL, SPARGE_ERR_ARG (n_kblocks < 1),
+ * SPARGE_ERR_TOPK. Makes no HIP call. */
+int sparge_topk_count(int64_t n_kblocks, double topk, int64_t *k_out);
+
+/* Bytes of device workspace that sparge_attn_topk (topk in (0,1]) or
+ * block_sparse_attn (topk < 0: an arbitrary user mask) needs for this shape.
+ * Returns 0 for invalid arguments, and for block_sparse_attn with a NULL mask
+ * (dense attention needs no workspace, but the call accepts any workspace). */
+size_t sparge_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, double topk);
+
+/* Block-mean pooling (first step of mask prediction).
+ *   x          (B, H, N, D) bf16, strides x_strides (elements, B/H/N axes).
+ *   block_rows 128 for Q, 64 for K.
+ *   out        (B, H, ceil(N/block_rows), D) fp32, contiguous. Row i is the
+ *              mean of x rows [i*block_rows, min(N, (i+1)*block_rows)),
+ *              divided by the number of rows actually present.
+ * Errors: NULL, SHAPE, STRIDE, ARG, ALIAS (out overlapping x), LAUNCH. */
+int sparge_pool_blocks(const uint16_t *x, int64_t B, int64_t H, int64_t N, int64_t D,
+                       const int64_t x_strides[3], int block_rows, float *out, void *stream);
+
+/* Pooled-block scoring and per-row top-k selection.
+ *   qbar     (B, H, N_QB, D) fp32 contiguous (sparge_pool_blocks with 128).
+ *   kbar     (B, H, N_KB, D) fp32 contiguous (sparge_pool_blocks with 64).
+ *   topk     in (0, 1]; each row keeps k = sparge_topk_count(N_KB, topk) blocks.
+ *   scale    logit scale (<= 0: 1/sqrt(D)); s[i][j] = scale * qbar_i . kbar_j
+ *            in fp32. Selection ranks s, which ranks the row softmax the same way.
+ *   mask_id  optional (NULL allowed): (B, H, N_QB, N_KB) uint8 contiguous, 1 for
+ *            a kept block, 0 otherwise.
+ *   kv_idx   (B, H, N_QB, k) int32 contiguous: the kept key-block ids of each
+ *            row in ascending order.
+ *   kv_cnt   (B, H, N_QB) int32: k for every row.
+ * Ties in s go to the lower key-block index, so the result is deterministic.
+ * Errors: NULL, SHAPE (also N > SPARGE_MAX_PREDICT_N), TOPK, ALIAS, LAUNCH. */
+int sparge_predict_mask(const float *qbar, const float *kbar, int64_t B, int64_t H, int64_t N,
+                        int64_t D, double topk, float scale, uint8_t *mask_id, int32_t *kv_idx,
+                        int32_t *kv_cnt, void *stream);
+
+/* Mask compaction: each mask_id row becomes the ascending list of the key
+ * blocks it selects (any nonzero byte counts as selected).
+ *   mask_id  (B, H, N_QB, N_KB) uint8 contiguous.
+ *   kv_idx   (B, H, N_QB, N_KB) int32 contiguous; entries past kv_cnt are unspecified.
+ *   kv_cnt   (B, H, N_QB) int32.
+ * Errors: NULL, SHAPE, ALIAS, LAUNCH. */
+int sparge_compact_mask(const uint8_t *mask_id, int64_t B, int64_t H, int64_t N,
+                        int32_t *kv_idx, int32_t *kv_cnt, void *stream);
+
+/* Block-sparse attention from a compacted block list (the "apply" half of a
+ * predict-then-apply split; a list may be reused across calls).
+ *   kv_idx   (B, H, N_QB, ld_idx) int32: row r visits key blocks
+ *            kv_idx[r][0 .. kv_cnt[r]-1], each in [0, N_KB). NULL means dense
+ *            (every row visits all N_KB blocks; kv_cnt and ld_idx are ignored).
+ *   kv_cnt   (B, H, N_QB) int32, each in [0, ld_idx].
+ *   out      (B, H, N, D) bf16 with strides o_strides; rows with an empty list
+ *            are written as zeros.
+ * O[r] = sum_c softmax_c(scale * Q[r] . K[c]) V[c] over the keys c of the listed
+ * blocks (fp32 accumulation, probabilities rounded to bf16 before the PV
+ * product, output rounded to nearest-even bf16).
+ * Errors: NULL, SHAPE, STRIDE, ALIAS, ARG (ld_idx < 1), LAUNCH. */
+int sparge_attn_from_list(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                          const int32_t *kv_idx, const int32_t *kv_cnt, int64_t ld_idx,
+                          uint16_t *out, int64_t B, int64_t H, int64_t N, int64_t D,
+                          const int64_t q_strides[3], const int64_t k_strides[3],
+                          const int64_t v_strides[3], const int64_t o_strides[3], float scale,
+                          void *stream);
+
+/* Block-sparse attention with a given block mask
+ * (SpargeAttention Documentation, block_sparse_sage2_attn_cuda and "Mask
+ * Requirements"). mask_id is (B, H, N_QB, N_KB) uint8 contiguous with 0/1
+ * entries (nonzero counts as 1), or NULL for dense attention. The mask is
+ * compacted into the workspace, then attention runs over the listed tiles.
+ *   workspace   device buffer of at least sparge_workspace_bytes(B,H,N,D,-1).
+ * Errors: NULL, SHAPE, STRIDE, ALIAS, WORKSPACE, LAUNCH. */
+int block_sparse_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                      const uint8_t *mask_id, uint16_t *out, int64_t B, int64_t H, int64_t N,
+                      int64_t D, const int64_t q_strides[3], const int64_t k_strides[3],
+                      const int64_t v_strides[3], const int64_t o_strides[3], float scale,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* Top-k block-sparse attention, a drop-in for non-causal scaled dot-product
+ * attention (SpargeAttention Documentation, spas_sage2_attn_meansim_topk_cuda:
+ * higher topk favours accuracy, lower topk sparsity). Runs pooling,
+ * prediction and attention back to back on `stream`.
+ *   topk        in (0, 1].
+ *   scale       used both for the pooled scores and for attention (<= 0: 1/sqrt(D)).
+ *   mask_out    optional (NULL allowed): receives the predicted mask_id,
+ *               (B, H, N_QB, N_KB) uint8 contiguous.
+ *   workspace   device buffer of at least sparge_workspace_bytes(B,H,N,D,topk).
+ * Errors: NULL, SHAPE, TOPK, STRIDE, ALIAS, WORKSPACE, LAUNCH. */
+int sparge_attn_topk(const uint16_t *q, const uint16_t *k, const uint16_t *v, double topk,
+                     uint16_t *out, int64_t B, int64_t H, int64_t N, int64_t D,
+                     const int64_t q_strides[3], const int64_t k_strides[3],
+                     const int64_t v_strides[3], const int64_t o_strides[3], float scale,
+                     uint8_t *mask_out, void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARGE_H */

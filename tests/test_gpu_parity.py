@@ -1,0 +1,255 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Bars: pooled means within 1e-6 relative; masks bit-exact except rows whose
+pooled-logit gap at the top-k boundary is below 1e-5 (those only need a valid
+selection; the count is printed); attention outputs, with the oracle run on
+the GPU's own mask, within max-abs 2e-2 and mean-abs 2e-3; block lists and
+counts bit-exact.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_sparge_amd as sp
+import oracle
+import synth
+from gpu_harness import (assert_close, oracle_mask_parity, rand_qkv, to_dev, to_host_f64)
+
+pytestmark = pytest.mark.gpu
+
+F64 = synth.bf16_bits_to_f64
+
+# (B, H, N, D): several tiles with ragged query and key tails, plus aligned sizes.
+SMALL = [(1, 2, 1000, 128), (2, 3, 777, 64), (1, 2, 1024, 64), (1, 1, 384, 128), (1, 3, 200, 128)]
+EDGE_N = [1, 2, 63, 64, 65, 127, 128, 129, 191]
+
+
+def _dev(q, k, v):
+    return to_dev(q), to_dev(k), to_dev(v)
+
+
+@pytest.mark.parametrize("B,H,N,D", SMALL + [(1, 1, n, 64) for n in (1, 65, 129)])
+def test_pool_blocks(gpu_lib, B, H, N, D):
+    q, k, _ = rand_qkv(B, H, N, D, seed=N + D)
+    for x, rows in ((q, 128), (k, 64)):
+        got = sp.pool_blocks(to_dev(x), rows).cpu().numpy().astype(np.float64)
+        ref = oracle.pool_blocks(F64(x), rows)
+        assert got.shape == ref.shape
+        assert np.abs(got - ref).max() <= 1e-6 * max(1.0, np.abs(ref).max())
+
+
+@pytest.mark.parametrize("B,H,N,D", SMALL)
+@pytest.mark.parametrize("topk", [0.05, 0.3, 0.5, 1.0])
+def test_predict_mask_and_lists(gpu_lib, B, H, N, D, topk):
+    q, k, _ = rand_qkv(B, H, N, D, seed=7 * N + D, grid=None)
+    dq, dk = to_dev(q), to_dev(k)
+    qbar, kbar = sp.pool_blocks(dq, 128), sp.pool_blocks(dk, 64)
+    mask, idx, cnt = sp.predict_mask(qbar, kbar, N, topk)
+    torch.cuda.synchronize()
+    mask, idx, cnt = mask.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy()
+    kk = oracle.topk_count(mask.shape[-1], topk)
+    assert idx.shape[-1] == kk and (cnt == kk).all()
+    assert (mask.sum(-1) == kk).all()
+    ref_idx, ref_cnt = oracle.compact_mask(mask)
+    assert (ref_cnt == kk).all() and (idx == ref_idx[..., :kk]).all()
+    rep = oracle_mask_parity(lambda b, h: F64(q[b, h]), lambda b, h: F64(k[b, h]), topk, mask)
+    print("mask parity", rep)
+    assert rep["failures"] == 0
+
+
+def test_predict_ties_go_to_lower_index(gpu_lib):
+    """Bit-identical key blocks: the lower index must win the last kept slot."""
+    N, D = 1024, 64
+    q, k, _ = rand_qkv(1, 1, N, D, seed=11)
+    k[0, 0, 512:1024] = k[0, 0, 0:512]          # blocks 8..15 duplicate blocks 0..7
+    q[0, 0] = q[0, 0, :1].repeat(N, axis=0)     # every query block pools to the same row
+    for topk in (1 / 16, 3 / 16, 5 / 16, 0.5, 9 / 16):
+        qbar, kbar = sp.pool_blocks(to_dev(q), 128), sp.pool_blocks(to_dev(k), 64)
+        mask, _, _ = sp.predict_mask(qbar, kbar, N, topk)
+        ref = oracle.predict_mask(F64(q), F64(k), topk)["mask"]
+        assert (mask.cpu().numpy() == ref).all(), topk
+
+
+def _random_mask(B, H, N, density, seed, empty_rows=True):
+    rng = np.random.default_rng(seed)
+    shape = sp.mask_shape(B, H, N)
+    m = (rng.random(shape) < density).astype(np.uint8)
+    if empty_rows and shape[2] > 1:
+        m[:, :, 1, :] = 0                       # a query block with nothing selected
+    return m
+
+
+@pytest.mark.parametrize("B,H,N,D", SMALL)
+@pytest.mark.parametrize("density", [0.1, 0.5, 1.0])
+def test_block_sparse_attn_user_mask(gpu_lib, B, H, N, D, density):
+    q, k, v = rand_qkv(B, H, N, D, seed=3 * N + D)
+    m = _random_mask(B, H, N, density, seed=N)
+    out = sp.block_sparse_attn(*_dev(q, k, v), mask_id=torch.from_numpy(m).cuda())
+    got = to_host_f64(out)
+    ref = oracle.masked_attention(F64(q), F64(k), F64(v), m)
+    r = assert_close(got, ref, f"user mask {B, H, N, D, density}")
+    if m.shape[2] > 1:
+        assert (got[:, :, 128:256] == 0).all()   # empty row -> zeros
+    print(r)
+
+
+@pytest.mark.parametrize("B,H,N,D", SMALL)
+def test_dense_and_topk_one(gpu_lib, B, H, N, D):
+    q, k, v = rand_qkv(B, H, N, D, seed=5 * N + D)
+    dq, dk, dv = _dev(q, k, v)
+    dense = sp.block_sparse_attn(dq, dk, dv, mask_id=None)
+    ones = sp.block_sparse_attn(dq, dk, dv, mask_id=torch.ones(sp.mask_shape(B, H, N), dtype=torch.uint8, device="cuda"))
+    top1, mask = sp.attn_topk(dq, dk, dv, topk=1.0, return_mask=True)
+    torch.cuda.synchronize()
+    assert mask.cpu().numpy().all()
+    # the same tiles in the same order: bit-identical
+    assert torch.equal(dense.view(torch.int16), ones.view(torch.int16))
+    assert torch.equal(dense.view(torch.int16), top1.view(torch.int16))
+    t = lambda a: torch.from_numpy(F64(a))
+    ref = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v)).numpy()
+    assert_close(to_host_f64(dense), ref, "dense vs SDPA")
+
+
+@pytest.mark.parametrize("N", EDGE_N)
+@pytest.mark.parametrize("D", [64, 128])
+def test_edge_lengths(gpu_lib, N, D):
+    q, k, v = rand_qkv(1, 2, N, D, seed=N * 3 + D)
+    dq, dk, dv = _dev(q, k, v)
+    out, mask = sp.attn_topk(dq, dk, dv, topk=0.5, return_mask=True)
+    m = mask.cpu().numpy()
+    ref = oracle.masked_attention(F64(q), F64(k), F64(v), m)
+    assert_close(to_host_f64(out), ref, f"edge N={N}")
+    rep = oracle_mask_parity(lambda b, h: F64(q[b, h]), lambda b, h: F64(k[b, h]), 0.5, m)
+    assert rep["failures"] == 0
+
+
+@pytest.mark.parametrize("B,H,N,D", SMALL)
+@pytest.mark.parametrize("topk", [0.2, 0.5])
+def test_attn_topk_end_to_end(gpu_lib, B, H, N, D, topk):
+    q, k, v = rand_qkv(B, H, N, D, seed=9 * N + D, q_scale=1 / math.sqrt(D))
+    out, mask = sp.attn_topk(*_dev(q, k, v), topk=topk, return_mask=True)
+    m = mask.cpu().numpy()
+    rep = oracle_mask_parity(lambda b, h: F64(q[b, h]), lambda b, h: F64(k[b, h]), topk, m)
+    assert rep["failures"] == 0, rep
+    ref = oracle.masked_attention(F64(q), F64(k), F64(v), m)
+    print(assert_close(to_host_f64(out), ref, "attn_topk"), rep)
+
+
+def test_strided_layouts_and_scale(gpu_lib):
+    B, H, N, D = 2, 3, 700, 128
+    q, k, v = rand_qkv(B, H, N, D, seed=21)
+    dq, dk, dv = _dev(q, k, v)
+    # (B, N, H, D) storage viewed as (B, H, N, D), like a fused projection's output
+    tq, tk, tv = (x.transpose(1, 2).contiguous().transpose(1, 2) for x in (dq, dk, dv))
+    assert tq.stride() != dq.stride()
+    out_t = torch.empty(B, N, H, D, dtype=torch.bfloat16, device="cuda").transpose(1, 2)
+    m = torch.from_numpy(_random_mask(B, H, N, 0.4, seed=3)).cuda()
+    a = sp.block_sparse_attn(dq, dk, dv, mask_id=m, scale=0.05)
+    b = sp.block_sparse_attn(tq, tk, tv, mask_id=m, scale=0.05, out=out_t)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.contiguous().view(torch.int16))
+    ref = oracle.masked_attention(F64(q), F64(k), F64(v), m.cpu().numpy(), scale=0.05)
+    assert_close(to_host_f64(a), ref, "scale=0.05")
+
+
+def test_deterministic(gpu_lib):
+    wl = synth.WORKLOADS[0]
+    q, k, v = synth.make_qkv(wl)
+    dq, dk, dv = _dev(q, k, v)
+    o1, m1 = sp.attn_topk(dq, dk, dv, topk=0.5, return_mask=True)
+    o2, m2 = sp.attn_topk(dq, dk, dv, topk=0.5, return_mask=True)
+    torch.cuda.synchronize()
+    assert torch.equal(m1, m2) and torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_from_list_reuse(gpu_lib):
+    """A predicted list applied with attn_from_list equals the one-call top-k path."""
+    B, H, N, D = 1, 4, 2000, 128
+    q, k, v = rand_qkv(B, H, N, D, seed=33, q_scale=1 / math.sqrt(D))
+    dq, dk, dv = _dev(q, k, v)
+    mask, idx, cnt = sp.predict_mask(sp.pool_blocks(dq, 128), sp.pool_blocks(dk, 64), N, 0.3)
+    a = sp.attn_from_list(dq, dk, dv, idx, cnt)
+    b = sp.attn_topk(dq, dk, dv, topk=0.3)
+    c = sp.block_sparse_attn(dq, dk, dv, mask_id=mask)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
+def test_predict_at_length_limit(gpu_lib):
+    """The longest sequence the prediction accepts (one 48 KB score row per workgroup)."""
+    N, D = 786432, 64
+    wl = synth.custom(1, 1, N, D, config_id=300)
+    q, k = synth.make_tensor(wl, "q"), synth.make_tensor(wl, "k")
+    qbar, kbar = sp.pool_blocks(to_dev(q), 128), sp.pool_blocks(to_dev(k), 64)
+    mask, idx, cnt = sp.predict_mask(qbar, kbar, N, 0.05)
+    m = mask.cpu().numpy()
+    kk = oracle.topk_count(N // 64, 0.05)
+    assert (m.sum(-1) == kk).all() and (cnt.cpu().numpy() == kk).all()
+    rep = oracle_mask_parity(lambda b, h: F64(q[b, h]), lambda b, h: F64(k[b, h]), 0.05, m)
+    print(rep)
+    assert rep["failures"] == 0
+    with pytest.raises(sp.SpargeArgumentError):
+        sp.predict_mask(torch.zeros(1, 1, 6145, D, device="cuda"),
+                        torch.zeros(1, 1, 12289, D, device="cuda"), N + 64, 0.05)
+
+
+# ------------------------------------------------------------ full-size workloads
+
+def _sample_rows(N, rng, n=48):
+    tail = np.arange(max(0, N - 16), N)
+    head = np.arange(0, min(N, 8))
+    mid = rng.choice(N, size=min(N, n), replace=False)
+    return np.unique(np.concatenate([head, mid, tail]))
+
+
+WORKLOAD_CASES = [(0, 0.5), (1, 0.5), (2, 0.4), (3, 0.3), (4, 0.1)]
+
+
+@pytest.mark.parametrize("cfg,topk", WORKLOAD_CASES, ids=[f"cfg{c}-topk{t}" for c, t in WORKLOAD_CASES])
+def test_workload_parity(gpu_lib, cfg, topk):
+    """Every mask row at the workload's full size; outputs on sampled rows of sampled heads."""
+    wl = synth.WORKLOADS[cfg]
+    print(f"workload {wl.describe()} topk={topk}", flush=True)
+    q, k, v = synth.make_qkv(wl, seed=0)
+    dq, dk, dv = _dev(q, k, v)
+    out, mask = sp.attn_topk(dq, dk, dv, topk=topk, return_mask=True)
+    torch.cuda.synchronize()
+    m = mask.cpu().numpy()
+    rep = oracle_mask_parity(lambda b, h: F64(q[b, h]), lambda b, h: F64(k[b, h]), topk, m)
+    print("mask parity", rep, flush=True)
+    assert rep["failures"] == 0
+    rng = np.random.default_rng(cfg)
+    heads = sorted({(0, 0), (wl.B - 1, wl.H // 2), (wl.B - 1, wl.H - 1)})
+    outs = out.view(torch.int16)
+    worst = {"max_abs": 0.0, "mean_abs": 0.0}
+    for b, h in heads:
+        rows = _sample_rows(wl.N, rng) if cfg else np.arange(wl.N)
+        got = synth.bf16_bits_to_f64(outs[b, h, torch.from_numpy(rows).cuda()].cpu().numpy().view(np.uint16))
+        ref = oracle.masked_attention_rows(F64(q[b, h]), F64(k[b, h]), F64(v[b, h]), m[b, h], rows)
+        r = assert_close(got, ref, f"cfg{cfg} head {(b, h)}")
+        worst = {key: max(worst[key], r[key]) for key in worst}
+    print("output parity", worst, flush=True)
+
+
+@pytest.mark.parametrize("topk", [0.1, 0.2, 0.5, 1.0])
+def test_wan14b_topk_sweep(gpu_lib, topk):
+    """The other points of the 720p Wan2.1-14B sweep: counts, one head's mask, sampled outputs."""
+    wl = synth.WORKLOADS[3]
+    heads = [(0, 0), (0, 39)]
+    q, k, v = synth.make_qkv(wl, seed=0)
+    out, mask = sp.attn_topk(*_dev(q, k, v), topk=topk, return_mask=True)
+    m = mask.cpu().numpy()
+    kk = oracle.topk_count(m.shape[-1], topk)
+    assert (m.sum(-1) == kk).all()
+    rng = np.random.default_rng(int(topk * 10))
+    for b, h in heads:
+        pr = oracle.predict_mask(F64(q[b, h])[None, None], F64(k[b, h])[None, None], topk)
+        rep = oracle.mask_parity(pr["logits"], pr["mask"], m[b, h][None, None], kk)
+        assert rep["failures"] == 0, rep
+        rows = _sample_rows(wl.N, rng, 24)
+        got = synth.bf16_bits_to_f64(out.view(torch.int16)[b, h, torch.from_numpy(rows).cuda()].cpu().numpy().view(np.uint16))
+        ref = oracle.masked_attention_rows(F64(q[b, h]), F64(k[b, h]), F64(v[b, h]), m[b, h], rows)
+        assert_close(got, ref, f"topk {topk} head {(b, h)}")
