@@ -53,13 +53,20 @@ def parse():
     return p.parse_args()
 
 
-def effective_flops(mask: np.ndarray, N: int, D: int) -> float:
-    """4*D * sum over kept tiles of (valid query rows) x (valid keys)."""
-    qb, kb = mask.shape[-2:]
+def block_rows_cols(N: int):
+    """Valid query rows per query block and valid keys per key block."""
+    qb, kb = -(-N // 128), -(-N // 64)
     rows = np.full(qb, 128.0)
     rows[-1] = N - 128 * (qb - 1)
     cols = np.full(kb, 64.0)
     cols[-1] = N - 64 * (kb - 1)
+    return rows, cols
+
+
+def effective_flops(mask: np.ndarray, N: int, D: int) -> float:
+    """4*D * sum over kept tiles of (valid query rows) x (valid keys); mask (..., Qb, Kb)."""
+    rows, cols = block_rows_cols(N)
+    qb, kb = mask.shape[-2:]
     per_row = mask.reshape(-1, qb, kb).astype(np.float64) @ cols        # (BH, qb)
     return 4.0 * D * float((per_row @ rows).sum())
 
@@ -123,8 +130,8 @@ def cpu_baseline(wl, q, k, v, topk, budget_s):
             t1 = time.perf_counter()
             oracle.masked_attention_rows(qh, kh, vh, m, rows)
             t_attn += time.perf_counter() - t1
-            flops += effective_flops(m[done:done + 1][None], N, D) if done < qb - 1 else \
-                effective_flops(m[None, -1:], N, D) * (len(rows) / 128.0)
+            brows, bcols = block_rows_cols(N)
+            flops += 4.0 * D * brows[done] * float(m[done].astype(np.float64) @ bcols)
             done += 1
         bh = wl.B * wl.H
         full_attn_s = t_attn * (qb / done) * bh
