@@ -17,6 +17,7 @@ namespace {
 
 constexpr int64_t kMaxDim = int64_t(1) << 40;   // guards the size arithmetic below against overflow
 constexpr size_t kAlign = 256;
+constexpr int64_t kMaxRowStride = int64_t(1) << 24;   // elements between consecutive tokens
 
 bool valid_d(int64_t D) { return D == 64 || D == 128; }
 
@@ -115,6 +116,9 @@ int check_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t
   if (int rc = check_shape(B, H, N, D)) return rc;
   for (const int64_t* s : {qs, ks, vs, os})
     if (int rc = check_strides(s)) return rc;
+  // the attention kernel addresses the rows of one 64-key tile with 32-bit byte offsets
+  for (const int64_t* s : {qs, ks, vs})
+    if (s[2] > kMaxRowStride) return SPARGE_ERR_STRIDE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SPARGE_ERR_STRIDE;
   if (!non_overlapping(B, H, N, D, os)) return SPARGE_ERR_STRIDE;
   const Range ro = range_bf16(out, B, H, N, D, os);

@@ -7,52 +7,72 @@
 // sum l per query row and rescales the output accumulator in registers.
 //
 // Work decomposition
-//   one workgroup = one query block of one head, 4 wavefronts x 32 query rows.
+//   One workgroup = one query block of one head: 4 wavefronts x 32 query rows.
 //   Per 64-key tile, each wavefront computes S^T = K_tile Q_w^T (64 x 32) with
-//   v_mfma_f32_32x32x16_bf16, so every lane ends up owning one query row
-//   (lane % 32) and 32 of the tile's 64 scores. Row max / row sum need a single
-//   exchange with the partner lane (lane ^ 32). The probabilities, rounded to
-//   bf16, are already laid out as the B operand of O^T += V^T P^T, so they never
-//   leave registers. V^T operands come straight from the row-major V tile with
-//   the gfx950 transpose read ds_read_b64_tr_b16.
-//   K rows are read in a permuted order (sigma below) so that the S^T
-//   accumulator registers hold consecutive keys, matching the PV operand order.
+//   v_mfma_f32_32x32x16_bf16, so every lane owns one query row (lane % 32) and
+//   32 of the tile's 64 scores; row max and row sum need one exchange with the
+//   partner lane (lane ^ 32). The probabilities, rounded to bf16, are already
+//   laid out as the B operand of O^T += V^T P^T, so they never leave registers.
+//   V^T operands come straight from the row-major V tile through the gfx950
+//   transpose read ds_read_b64_tr_b16. K rows are read in a permuted order
+//   (sigma below) so that the S^T accumulators hold consecutive keys, which is
+//   the key order the PV operands need.
+//
+// Softmax
+//   Base 2 with the scale folded into one FMA. The running max is raised only
+//   when a row's tile max exceeds it by more than 2^8 (probabilities then stay
+//   below 256, exact in fp32 and as accurate in bf16), so the output
+//   accumulator is rescaled on a handful of tiles instead of every tile. Row
+//   sums add the bf16-rounded probabilities with v_dot2_f32_bf16, so they match
+//   the weights the PV product actually used.
 //
 // Memory
-//   Q rows stay in registers for the whole walk. K and V tiles are staged
-//   through LDS, double buffered: the global loads for tile t+1 are issued
-//   before tile t is computed and land in the other LDS buffer afterwards
-//   (one barrier per tile). Row pitches are padded (K: +16 B, V: +64 B) so the
-//   two LDS read patterns spread over the banks.
+//   Q rows stay in registers for the whole walk. K and V tiles go global -> LDS
+//   with global_load_lds_dwordx4 (no registers, no LDS write instructions),
+//   double buffered: tile t+1 is requested before tile t is computed, one
+//   barrier per tile. Tiles are stored unpadded (64 KB of LDS per workgroup at
+//   D=128, so two workgroups share a CU) with 16-byte chunks XOR-swizzled per
+//   row: K so that the 16 rows one A-operand read touches hit distinct banks,
+//   V so that the 4 rows of one transpose read do.
 //   Workgroups are numbered so that each of the 8 XCDs (each with its own L2)
-//   walks a contiguous range of query blocks of the same head, and all XCDs
-//   move through the heads together, keeping one head's K/V hot in the
-//   last-level cache while neighbouring query blocks share tiles in L2.
+//   walks a contiguous range of query blocks of one head while all XCDs move
+//   through the heads together: one head's K/V stays hot in the last-level
+//   cache and neighbouring query blocks, whose lists overlap, share L2.
 #include "common.h"
 
 namespace sparge {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void global_cvoid;
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleSlack = 8.0f;   // log2 headroom before the running max is raised
 
 template <int D>
 struct Cfg {
-  static constexpr int kKPitch = D * 2 + 16;          // bytes per K row in LDS
-  static constexpr int kVPitch = D * 2 + 64;          // bytes per V row in LDS
-  static constexpr int kKBytes = kKBlock * kKPitch;
-  static constexpr int kVBytes = kKBlock * kVPitch;
-  static constexpr int kStage = kKBytes + kVBytes;
-  static constexpr int kLds = 2 * kStage;
-  static constexpr int kChunksPerRow = D / 8;         // 16-byte chunks per row
-  static constexpr int kChunksPerThread = kKBlock * kChunksPerRow / 256;
-  static constexpr int kSteps = D / 16;               // k-steps of the QK^T product
-  static constexpr int kDChunks = D / 32;             // 32-wide column chunks of O
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kChunks = D / 8;                     // 16-byte chunks per row
+  static constexpr int kTile = kKBlock * kRowBytes;         // one K or V tile in LDS
+  static constexpr int kStage = 2 * kTile;                  // K tile then V tile
+  static constexpr int kLds = 2 * kStage;                   // double buffered
+  static constexpr int kRowsPerInst = 64 / kChunks;         // rows one wavefront load fills
+  static constexpr int kInstPerWave = kKBlock / (4 * kRowsPerInst);
+  static constexpr int kSteps = D / 16;                     // k-steps of QK^T
+  static constexpr int kDChunks = D / 32;                   // 32-column chunks of O
 };
+
+// Chunk swizzles (XOR on the 16-byte chunk index within a row).
+template <int D>
+__device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int swz_v(int r) { return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2); }
 
 struct Params {
   const uint16_t* q;
@@ -77,12 +97,13 @@ __device__ __forceinline__ int sigma(int m) {
 }
 
 // Key block visited at step tt. An id outside [0, n_kb) maps to a block past
-// the end of the sequence: its keys load as zeros and are masked out, so a
-// corrupt list entry contributes nothing instead of reading out of bounds.
-__device__ __forceinline__ int64_t block_id(const int32_t* list, int tt, int64_t n_kb) {
-  if (!list) return tt;
-  const int64_t j = list[tt];
+// the end of the sequence whose keys are all masked, so a corrupt list entry
+// contributes nothing instead of reading out of bounds.
+__device__ __forceinline__ int64_t sanitize_id(int64_t j, int64_t n_kb) {
   return (j >= 0 && j < n_kb) ? j : n_kb;
+}
+__device__ __forceinline__ int64_t block_id(const int32_t* list, int tt, int64_t n_kb) {
+  return list ? sanitize_id(list[tt], n_kb) : tt;
 }
 
 __device__ __forceinline__ uint4 load16(const uint16_t* p) {
@@ -90,44 +111,9 @@ __device__ __forceinline__ uint4 load16(const uint16_t* p) {
 }
 
 template <int D>
-__device__ __forceinline__ void load_tile(const uint16_t* kh, const uint16_t* vh, int64_t kn,
-                                          int64_t vn, int64_t N, int64_t j, int t,
-                                          uint4 (&kr)[Cfg<D>::kChunksPerThread],
-                                          uint4 (&vr)[Cfg<D>::kChunksPerThread]) {
-#pragma unroll
-  for (int e = 0; e < Cfg<D>::kChunksPerThread; ++e) {
-    const int c = t + 256 * e;
-    const int row = c / Cfg<D>::kChunksPerRow;
-    const int col = (c % Cfg<D>::kChunksPerRow) * 8;
-    const int64_t key = j * kKBlock + row;
-    if (key < N) {
-      kr[e] = load16(kh + key * kn + col);
-      vr[e] = load16(vh + key * vn + col);
-    } else {
-      kr[e] = make_uint4(0, 0, 0, 0);
-      vr[e] = make_uint4(0, 0, 0, 0);
-    }
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void store_tile(char* stage, int t,
-                                           const uint4 (&kr)[Cfg<D>::kChunksPerThread],
-                                           const uint4 (&vr)[Cfg<D>::kChunksPerThread]) {
-#pragma unroll
-  for (int e = 0; e < Cfg<D>::kChunksPerThread; ++e) {
-    const int c = t + 256 * e;
-    const int row = c / Cfg<D>::kChunksPerRow;
-    const int colb = (c % Cfg<D>::kChunksPerRow) * 16;
-    *reinterpret_cast<uint4*>(stage + row * Cfg<D>::kKPitch + colb) = kr[e];
-    *reinterpret_cast<uint4*>(stage + Cfg<D>::kKBytes + row * Cfg<D>::kVPitch + colb) = vr[e];
-  }
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(Params p) {
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) char lds[C::kLds];
+  __shared__ __attribute__((aligned(1024))) char lds[C::kLds];
 
   // Workgroup -> (head, query block). Consecutive workgroup ids go to
   // consecutive XCDs; XCD x owns query blocks [x*per, (x+1)*per) of every head.
@@ -176,38 +162,90 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(Params p) {
   float m = -INFINITY;
   float l = 0.f;
 
-  const int sig = sigma(n);
-  // transpose-read lane geometry for the V^T operand
-  const int tr_key = 8 * g + ((lane & 15) >> 2);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // ---- per-lane LDS geometry (constant over the walk)
+  // K A-operand: row sigma(n) (+32 for the second half), logical chunk 2s + g.
+  const int krow = sigma(n);
+  const int kx = swz_k<D>(krow);
+  int koff[C::kSteps];
+#pragma unroll
+  for (int s = 0; s < C::kSteps; ++s) koff[s] = krow * C::kRowBytes + 16 * ((2 * s + g) ^ kx);
+  // V transpose read: row 16u + 8g + 4r + (lane%16)/4, logical chunk 4cc + lcx, half (lane & 1).
+  const int vrow = 8 * g + ((lane & 15) >> 2);
+  const int vx = swz_v<D>(vrow);
+  const int lcx = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  int voff[C::kDChunks];
+#pragma unroll
+  for (int cc = 0; cc < C::kDChunks; ++cc)
+    voff[cc] = vrow * C::kRowBytes + 16 * ((4 * cc + lcx) ^ vx) + 8 * (lane & 1);
+
+  // ---- global -> LDS: wavefront load e fills rows [r0, r0 + kRowsPerInst) of a tile.
+  // Per-lane byte offsets from the tile's first row are fixed; the tile base is scalar.
+  uint32_t ld_koff[C::kInstPerWave], ld_voff[C::kInstPerWave];
+  int ld_row[C::kInstPerWave];
+#pragma unroll
+  for (int e = 0; e < C::kInstPerWave; ++e) {
+    const int inst = wave * C::kInstPerWave + e;
+    const int r = inst * C::kRowsPerInst + lane / C::kChunks;
+    const int pc = lane % C::kChunks;
+    ld_row[e] = r;
+    ld_koff[e] = static_cast<uint32_t>((r * p.ks.n + 8 * (pc ^ swz_k<D>(r))) * 2);
+    ld_voff[e] = static_cast<uint32_t>((r * p.vs.n + 8 * (pc ^ swz_v<D>(r))) * 2);
+  }
+  const uint32_t lds_base = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds));
+  auto issue_tile = [&](int64_t j, int stage) {
+    const char* kb = reinterpret_cast<const char*>(kh + j * kKBlock * p.ks.n);
+    const char* vb = reinterpret_cast<const char*>(vh + j * kKBlock * p.vs.n);
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_base + stage * C::kStage +
+                                                       wave * C::kInstPerWave * 1024);
+    if (j * kKBlock + kKBlock <= p.N) {
+#pragma unroll
+      for (int e = 0; e < C::kInstPerWave; ++e) {
+        __builtin_amdgcn_global_load_lds((global_cvoid*)(kb + ld_koff[e]),
+                                         (lds_void*)(uintptr_t)(dst + e * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((global_cvoid*)(vb + ld_voff[e]),
+                                         (lds_void*)(uintptr_t)(dst + C::kTile + e * 1024), 16, 0, 0);
+      }
+    } else {
+      // ragged or invalid block: rows past N re-read the last row (masked later)
+#pragma unroll
+      for (int e = 0; e < C::kInstPerWave; ++e) {
+        const int64_t key = j * kKBlock + ld_row[e];
+        const int64_t back = key < p.N ? 0 : key - (p.N - 1);
+        __builtin_amdgcn_global_load_lds(
+            (global_cvoid*)(kb + ld_koff[e] - back * p.ks.n * 2), (lds_void*)(uintptr_t)(dst + e * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(
+            (global_cvoid*)(vb + ld_voff[e] - back * p.vs.n * 2), (lds_void*)(uintptr_t)(dst + C::kTile + e * 1024), 16, 0, 0);
+      }
+    }
+  };
 
   if (cnt > 0) {
-    uint4 kr[C::kChunksPerThread], vr[C::kChunksPerThread];
-    load_tile<D>(kh, vh, p.ks.n, p.vs.n, p.N, block_id(list, 0, p.n_kb), t, kr, vr);
-    store_tile<D>(lds, t, kr, vr);
+    int64_t j = block_id(list, 0, p.n_kb);
+    int64_t j_next = cnt > 1 ? block_id(list, 1, p.n_kb) : 0;
+    issue_tile(j, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
     for (int tt = 0; tt < cnt; ++tt) {
-      char* cur = lds + (tt & 1) * C::kStage;
-      const bool has_next = tt + 1 < cnt;
-      if (has_next) load_tile<D>(kh, vh, p.ks.n, p.vs.n, p.N, block_id(list, tt + 1, p.n_kb), t, kr, vr);
-      const int64_t j = block_id(list, tt, p.n_kb);
+      const char* cur = lds + (tt & 1) * C::kStage;
+      if (tt + 1 < cnt) issue_tile(j_next, (tt + 1) & 1);
+      // fetch the id two tiles ahead now; it is only checked and used after this tile
+      const int32_t raw_after = (tt + 2 < cnt) ? (list ? list[tt + 2] : tt + 2) : 0;
 
       // S^T = K Q^T for keys [0, 32) and [32, 64) of the tile.
       f32x16 s0, s1;
 #pragma unroll
       for (int i = 0; i < 16; ++i) { s0[i] = 0.f; s1[i] = 0.f; }
-      const char* krow0 = cur + sig * C::kKPitch + 16 * g;
-      const char* krow1 = krow0 + 32 * C::kKPitch;
 #pragma unroll
       for (int s = 0; s < C::kSteps; ++s) {
-        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(krow0 + 32 * s);
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(krow1 + 32 * s);
+        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(cur + koff[s]);
+        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(cur + koff[s] + 32 * C::kRowBytes);
         s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[s], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[s], s1, 0, 0, 0);
       }
 
-      // Keys past N in a ragged last block take no weight.
+      // Keys past N in a ragged (or invalid) block take no weight.
       if (j * kKBlock + kKBlock > p.N) {
         const int64_t lim = p.N - j * kKBlock;
 #pragma unroll
@@ -218,45 +256,52 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(Params p) {
         }
       }
 
-      // Online softmax in base 2.
-      float mx = s0[0];
+      // Row max of the tile (both partner lanes end with the same value).
+      float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s0[i]);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s1[i]);
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m, mx * p.c);
-      // A fully masked first tile (possible only for invalid list entries) keeps
-      // m at -inf; subtracting 0 instead then yields zero weights, not NaN.
-      const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m - m_ref);
-      m = m_new;
+      const float mt = mx * p.c;
+      if (__builtin_amdgcn_ballot_w64(mt > m + kRescaleSlack)) {
+        const float m_new = fmaxf(m, mt);
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);   // 0 on the first tile
+        l *= alpha;
+#pragma unroll
+        for (int cc = 0; cc < C::kDChunks; ++cc)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[cc][i] *= alpha;
+        m = m_new;
+      }
+      // m stays -inf only while every key seen so far was masked (invalid ids);
+      // subtracting 0 then gives zero weights instead of NaN.
+      const float mref = (m == -INFINITY) ? 0.f : m;
 
       bf16x8 pb[4];
-      float rs = 0.f;
+      const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const __bf16 e0 = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s0[i], p.c, -m_ref)));
-        const __bf16 e1 = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s1[i], p.c, -m_ref)));
-        pb[i >> 3][i & 7] = e0;
-        pb[2 + (i >> 3)][i & 7] = e1;
-        rs += static_cast<float>(e0) + static_cast<float>(e1);
+      for (int i = 0; i < 16; i += 2) {
+        const f32x2 e0 = {__builtin_amdgcn_exp2f(fmaf(s0[i], p.c, -mref)),
+                          __builtin_amdgcn_exp2f(fmaf(s0[i + 1], p.c, -mref))};
+        const f32x2 e1 = {__builtin_amdgcn_exp2f(fmaf(s1[i], p.c, -mref)),
+                          __builtin_amdgcn_exp2f(fmaf(s1[i + 1], p.c, -mref))};
+        const bf16x2 b0 = __builtin_convertvector(e0, bf16x2);
+        const bf16x2 b1 = __builtin_convertvector(e1, bf16x2);
+        pb[i >> 3][i & 7] = b0[0];
+        pb[i >> 3][(i & 7) + 1] = b0[1];
+        pb[2 + (i >> 3)][i & 7] = b1[0];
+        pb[2 + (i >> 3)][(i & 7) + 1] = b1[1];
+        l = __builtin_amdgcn_fdot2_f32_bf16(b0, ones, l, false);
+        l = __builtin_amdgcn_fdot2_f32_bf16(b1, ones, l, false);
       }
-      l = l * alpha + rs;
-#pragma unroll
-      for (int cc = 0; cc < C::kDChunks; ++cc)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[cc][i] *= alpha;
 
       // O^T += V^T P^T over four 16-key steps.
-      const char* vt = cur + C::kKBytes;
+      const char* vt = cur + C::kTile;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const char* vrow = vt + (16 * u + tr_key) * C::kVPitch;
 #pragma unroll
         for (int cc = 0; cc < C::kDChunks; ++cc) {
-          const char* a_lo = vrow + (32 * cc + tr_col) * 2;
-          const char* a_hi = a_lo + 4 * C::kVPitch;
+          const char* a_lo = vt + (16 * u) * C::kRowBytes + voff[cc];
+          const char* a_hi = a_lo + 4 * C::kRowBytes;
           const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (lds_s16x4*)(__attribute__((address_space(3))) char*)(a_lo));
           const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -267,8 +312,12 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(Params p) {
         }
       }
 
-      if (has_next) store_tile<D>(lds + ((tt + 1) & 1) * C::kStage, t, kr, vr);
+      // This wavefront's loads of tile t+1 have landed; the barrier makes every
+      // wavefront's loads visible and frees the buffer just read.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
+      j = j_next;
+      j_next = sanitize_id(raw_after, p.n_kb);
     }
   }
 
