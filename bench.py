@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 4096 flop/clk x 2.4 GHz (MI355X dense bf16 MFMA)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector
+COPY_BYTES = 1 << 30         # calibration copy for the traffic counters
 METRIC = "block-sparse attn TFLOPS (effective + dense-equiv) & ms/call, N=75600 topk=0.3"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_wan14b-720p_topk0.3_traffic.json")
 ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_sparge_amd", "csrc", "attn_fwd.hip")
@@ -50,6 +51,8 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--kernels-only", action="store_true",
+                   help="launch each kernel once plus a plain copy of known size, for counter runs")
     return p.parse_args()
 
 
@@ -192,6 +195,22 @@ def main():
     eff = effective_flops(m, N, D)
     dense = 4.0 * B * H * N * N * D
     log(f"k={kk} of {m.shape[-1]} key blocks; effective {eff / 1e12:.2f} TFLOP, dense {dense / 1e12:.2f} TFLOP")
+
+    if args.kernels_only:
+        # one launch of each kernel and a device copy of COPY_BYTES (read + write),
+        # whose FETCH_SIZE / WRITE_SIZE readings calibrate the counters
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        sp.attn_from_list(dq, dk, dv, idx, cnt, out=out)
+        sp.pool_blocks(dq, 128)
+        sp.pool_blocks(dk, 64)
+        sp.predict_mask(qbar, kbar, N, topk)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"kernels_only": True, "copy_bytes": COPY_BYTES, "workload": wl.name,
+                          "topk": topk, "effective_flops": eff}), flush=True)
+        return
 
     for _ in range(args.warmup):
         step()

@@ -38,6 +38,8 @@
 //   walks a contiguous range of query blocks of one head while all XCDs move
 //   through the heads together: one head's K/V stays hot in the last-level
 //   cache and neighbouring query blocks, whose lists overlap, share L2.
+#include <type_traits>
+
 #include "common.h"
 
 namespace sparge {
@@ -106,6 +108,17 @@ __device__ __forceinline__ int64_t block_id(const int32_t* list, int tt, int64_t
   return list ? sanitize_id(list[tt], n_kb) : tt;
 }
 
+// Value of x in the partner lane (lane ^ 32) combined with x: v_permlane32_swap
+// hands lane l both x[l % 32] and x[l % 32 + 32].
+__device__ __forceinline__ float max_with_partner(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_with_partner(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ uint4 load16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
@@ -113,7 +126,12 @@ __device__ __forceinline__ uint4 load16(const uint16_t* p) {
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(1024))) char lds[C::kLds];
+  // Four separate LDS objects (not one array) so that waits for the loads
+  // filling one buffer are not imposed on reads of another.
+  __shared__ __attribute__((aligned(1024))) char lds_k0[C::kTile];
+  __shared__ __attribute__((aligned(1024))) char lds_k1[C::kTile];
+  __shared__ __attribute__((aligned(1024))) char lds_v0[C::kTile];
+  __shared__ __attribute__((aligned(1024))) char lds_v1[C::kTile];
 
   // Workgroup -> (head, query block). Consecutive workgroup ids go to
   // consecutive XCDs; XCD x owns query blocks [x*per, (x+1)*per) of every head.
@@ -134,16 +152,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   const uint16_t* vh = p.v + b * p.vs.b + h * p.vs.h;
   uint16_t* oh = p.o + b * p.os.b + h * p.os.h;
 
+  // The block list is read-only for the whole launch: read it through the
+  // scalar cache (constant address space), a few tiles ahead of its use.
+  typedef __attribute__((address_space(4))) const int32_t cint32;
   const int64_t row_id = bh * p.n_qb + qb;
   int cnt;
-  const int32_t* list = nullptr;
+  const cint32* list = nullptr;
   if (p.kv_idx) {
-    cnt = p.kv_cnt[row_id];
+    cnt = ((const cint32*)p.kv_cnt)[row_id];
     cnt = cnt < 0 ? 0 : (cnt > p.ld_idx ? static_cast<int>(p.ld_idx) : cnt);
-    list = p.kv_idx + row_id * p.ld_idx;
+    list = (const cint32*)(p.kv_idx + row_id * p.ld_idx);
   } else {
     cnt = static_cast<int>(p.n_kb);
   }
+  auto raw_id = [&](int i) -> int64_t { return (i < cnt) ? (list ? list[i] : i) : 0; };
 
   // Q^T operands: lane (n, g) holds query row qrow, columns 16s + 8g .. +7.
   const int64_t qrow = qb * kQBlock + wave * 32 + n;
@@ -191,138 +213,162 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
     ld_koff[e] = static_cast<uint32_t>((r * p.ks.n + 8 * (pc ^ swz_k<D>(r))) * 2);
     ld_voff[e] = static_cast<uint32_t>((r * p.vs.n + 8 * (pc ^ swz_v<D>(r))) * 2);
   }
-  const uint32_t lds_base = static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds));
-  auto issue_tile = [&](int64_t j, int stage) {
-    const char* kb = reinterpret_cast<const char*>(kh + j * kKBlock * p.ks.n);
-    const char* vb = reinterpret_cast<const char*>(vh + j * kKBlock * p.vs.n);
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_base + stage * C::kStage +
-                                                       wave * C::kInstPerWave * 1024);
+  // Rows past N (ragged or invalid block) re-read row N-1; their scores are masked.
+  auto issue = [&](int64_t j, const uint16_t* base, int64_t rs, const uint32_t (&off)[C::kInstPerWave],
+                   char* buf) {
+    const char* tb = reinterpret_cast<const char*>(base + j * kKBlock * rs);
     if (j * kKBlock + kKBlock <= p.N) {
 #pragma unroll
-      for (int e = 0; e < C::kInstPerWave; ++e) {
-        __builtin_amdgcn_global_load_lds((global_cvoid*)(kb + ld_koff[e]),
-                                         (lds_void*)(uintptr_t)(dst + e * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((global_cvoid*)(vb + ld_voff[e]),
-                                         (lds_void*)(uintptr_t)(dst + C::kTile + e * 1024), 16, 0, 0);
-      }
+      for (int e = 0; e < C::kInstPerWave; ++e)
+        __builtin_amdgcn_global_load_lds((global_cvoid*)(tb + off[e]),
+                                         (lds_void*)(buf + (wave * C::kInstPerWave + e) * 1024),
+                                         16, 0, 0);
     } else {
-      // ragged or invalid block: rows past N re-read the last row (masked later)
 #pragma unroll
       for (int e = 0; e < C::kInstPerWave; ++e) {
         const int64_t key = j * kKBlock + ld_row[e];
         const int64_t back = key < p.N ? 0 : key - (p.N - 1);
-        __builtin_amdgcn_global_load_lds(
-            (global_cvoid*)(kb + ld_koff[e] - back * p.ks.n * 2), (lds_void*)(uintptr_t)(dst + e * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(
-            (global_cvoid*)(vb + ld_voff[e] - back * p.vs.n * 2), (lds_void*)(uintptr_t)(dst + C::kTile + e * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((global_cvoid*)(tb + off[e] - back * rs * 2),
+                                         (lds_void*)(buf + (wave * C::kInstPerWave + e) * 1024),
+                                         16, 0, 0);
+      }
+    }
+  };
+
+  // S^T = K Q^T for keys [0, 32) and [32, 64) of a tile.
+  auto qk = [&](const char* kb, f32x16& s0, f32x16& s1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { s0[i] = 0.f; s1[i] = 0.f; }
+#pragma unroll
+    for (int s = 0; s < C::kSteps; ++s) {
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kb + koff[s]);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kb + koff[s] + 32 * C::kRowBytes);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[s], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[s], s1, 0, 0, 0);
+    }
+  };
+
+  // Keys past N in a ragged (or invalid) block take no weight.
+  auto mask_tail = [&](int64_t j, f32x16& s0, f32x16& s1) {
+    if (j * kKBlock + kKBlock > p.N) {
+      const int64_t lim = p.N - j * kKBlock;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kl = (i < 8) ? 8 * g + i : 16 + 8 * g + (i - 8);
+        if (kl >= lim) s0[i] = -INFINITY;
+        if (kl + 32 >= lim) s1[i] = -INFINITY;
+      }
+    }
+  };
+
+  // Row max of a tile; raises the running max (and rescales O, l) when the
+  // tile max exceeds it by more than the slack. Returns the max to subtract.
+  auto update_max = [&](const f32x16& s0, const f32x16& s1) -> float {
+    float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+    mx = max_with_partner(mx);
+    const float mt = mx * p.c;
+    if (__builtin_amdgcn_ballot_w64(mt > m + kRescaleSlack)) {
+      const float m_new = fmaxf(m, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);   // 0 on the first tile
+      l *= alpha;
+#pragma unroll
+      for (int cc = 0; cc < C::kDChunks; ++cc)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[cc][i] *= alpha;
+      m = m_new;
+    }
+    // m stays -inf only while every key seen so far was masked (invalid ids);
+    // subtracting 0 then gives zero weights instead of NaN.
+    return (m == -INFINITY) ? 0.f : m;
+  };
+
+  // Probabilities of a tile as bf16 PV operands, and their sum into l.
+  auto probs = [&](const f32x16& s0, const f32x16& s1, float mref, bf16x8 (&pb)[4]) {
+    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const f32x2 e0 = {__builtin_amdgcn_exp2f(fmaf(s0[i], p.c, -mref)),
+                        __builtin_amdgcn_exp2f(fmaf(s0[i + 1], p.c, -mref))};
+      const f32x2 e1 = {__builtin_amdgcn_exp2f(fmaf(s1[i], p.c, -mref)),
+                        __builtin_amdgcn_exp2f(fmaf(s1[i + 1], p.c, -mref))};
+      const bf16x2 b0 = __builtin_convertvector(e0, bf16x2);
+      const bf16x2 b1 = __builtin_convertvector(e1, bf16x2);
+      pb[i >> 3][i & 7] = b0[0];
+      pb[i >> 3][(i & 7) + 1] = b0[1];
+      pb[2 + (i >> 3)][i & 7] = b1[0];
+      pb[2 + (i >> 3)][(i & 7) + 1] = b1[1];
+      l = __builtin_amdgcn_fdot2_f32_bf16(b0, ones, l, false);
+      l = __builtin_amdgcn_fdot2_f32_bf16(b1, ones, l, false);
+    }
+  };
+
+  // O^T += V^T P^T over four 16-key steps.
+  auto pv = [&](const char* vt, const bf16x8 (&pb)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int cc = 0; cc < C::kDChunks; ++cc) {
+        const char* a_lo = vt + (16 * u) * C::kRowBytes + voff[cc];
+        const char* a_hi = a_lo + 4 * C::kRowBytes;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(__attribute__((address_space(3))) char*)(a_lo));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(__attribute__((address_space(3))) char*)(a_hi));
+        const s16x4 lohi[2] = {lo, hi};
+        const bf16x8 a = __builtin_bit_cast(bf16x8, lohi);
+        o[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[u], o[cc], 0, 0, 0);
       }
     }
   };
 
   if (cnt > 0) {
-    int64_t j = block_id(list, 0, p.n_kb);
-    int64_t j_next = cnt > 1 ? block_id(list, 1, p.n_kb) : 0;
-    issue_tile(j, 0);
+    // Double buffering: step t computes tile t from buffers t%2 while the
+    // loads of tile t+1 fill the other pair.
+    int64_t j0 = sanitize_id(raw_id(0), p.n_kb);
+    int64_t j1 = sanitize_id(raw_id(1), p.n_kb);
+    issue(j0, kh, p.ks.n, ld_koff, lds_k0);
+    issue(j0, vh, p.vs.n, ld_voff, lds_v0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    for (int tt = 0; tt < cnt; ++tt) {
-      const char* cur = lds + (tt & 1) * C::kStage;
-      if (tt + 1 < cnt) issue_tile(j_next, (tt + 1) & 1);
-      // fetch the id two tiles ahead now; it is only checked and used after this tile
-      const int32_t raw_after = (tt + 2 < cnt) ? (list ? list[tt + 2] : tt + 2) : 0;
-
-      // S^T = K Q^T for keys [0, 32) and [32, 64) of the tile.
-      f32x16 s0, s1;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) { s0[i] = 0.f; s1[i] = 0.f; }
-#pragma unroll
-      for (int s = 0; s < C::kSteps; ++s) {
-        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(cur + koff[s]);
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(cur + koff[s] + 32 * C::kRowBytes);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[s], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[s], s1, 0, 0, 0);
+    auto step = [&](auto parity, int tt) {
+      constexpr int P = decltype(parity)::value;
+      char* k_cur = P ? lds_k1 : lds_k0;
+      char* v_cur = P ? lds_v1 : lds_v0;
+      char* k_fill = P ? lds_k0 : lds_k1;
+      char* v_fill = P ? lds_v0 : lds_v1;
+      const bool more = tt + 1 < cnt;
+      if (more) {
+        issue(j1, kh, p.ks.n, ld_koff, k_fill);
+        issue(j1, vh, p.vs.n, ld_voff, v_fill);
       }
-
-      // Keys past N in a ragged (or invalid) block take no weight.
-      if (j * kKBlock + kKBlock > p.N) {
-        const int64_t lim = p.N - j * kKBlock;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kl = (i < 8) ? 8 * g + i : 16 + 8 * g + (i - 8);
-          if (kl >= lim) s0[i] = -INFINITY;
-          if (kl + 32 >= lim) s1[i] = -INFINITY;
-        }
-      }
-
-      // Row max of the tile (both partner lanes end with the same value).
-      float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mt = mx * p.c;
-      if (__builtin_amdgcn_ballot_w64(mt > m + kRescaleSlack)) {
-        const float m_new = fmaxf(m, mt);
-        const float alpha = __builtin_amdgcn_exp2f(m - m_new);   // 0 on the first tile
-        l *= alpha;
-#pragma unroll
-        for (int cc = 0; cc < C::kDChunks; ++cc)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[cc][i] *= alpha;
-        m = m_new;
-      }
-      // m stays -inf only while every key seen so far was masked (invalid ids);
-      // subtracting 0 then gives zero weights instead of NaN.
-      const float mref = (m == -INFINITY) ? 0.f : m;
-
+      const int32_t raw2 = static_cast<int32_t>(raw_id(tt + 2));
+      f32x16 sa, sb;
+      qk(k_cur, sa, sb);
+      mask_tail(j0, sa, sb);
+      const float mref = update_max(sa, sb);
       bf16x8 pb[4];
-      const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const f32x2 e0 = {__builtin_amdgcn_exp2f(fmaf(s0[i], p.c, -mref)),
-                          __builtin_amdgcn_exp2f(fmaf(s0[i + 1], p.c, -mref))};
-        const f32x2 e1 = {__builtin_amdgcn_exp2f(fmaf(s1[i], p.c, -mref)),
-                          __builtin_amdgcn_exp2f(fmaf(s1[i + 1], p.c, -mref))};
-        const bf16x2 b0 = __builtin_convertvector(e0, bf16x2);
-        const bf16x2 b1 = __builtin_convertvector(e1, bf16x2);
-        pb[i >> 3][i & 7] = b0[0];
-        pb[i >> 3][(i & 7) + 1] = b0[1];
-        pb[2 + (i >> 3)][i & 7] = b1[0];
-        pb[2 + (i >> 3)][(i & 7) + 1] = b1[1];
-        l = __builtin_amdgcn_fdot2_f32_bf16(b0, ones, l, false);
-        l = __builtin_amdgcn_fdot2_f32_bf16(b1, ones, l, false);
+      probs(sa, sb, mref, pb);
+      pv(v_cur, pb);
+      j0 = j1;
+      j1 = sanitize_id(raw2, p.n_kb);
+      if (more) {
+        // This wavefront's loads of tile t+1 have landed; the barrier makes
+        // every wavefront's loads visible and frees the buffers just read.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
       }
-
-      // O^T += V^T P^T over four 16-key steps.
-      const char* vt = cur + C::kTile;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-#pragma unroll
-        for (int cc = 0; cc < C::kDChunks; ++cc) {
-          const char* a_lo = vt + (16 * u) * C::kRowBytes + voff[cc];
-          const char* a_hi = a_lo + 4 * C::kRowBytes;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)(__attribute__((address_space(3))) char*)(a_lo));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)(__attribute__((address_space(3))) char*)(a_hi));
-          const s16x4 lohi[2] = {lo, hi};
-          const bf16x8 a = __builtin_bit_cast(bf16x8, lohi);
-          o[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[u], o[cc], 0, 0, 0);
-        }
-      }
-
-      // This wavefront's loads of tile t+1 have landed; the barrier makes every
-      // wavefront's loads visible and frees the buffer just read.
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      j = j_next;
-      j_next = sanitize_id(raw_after, p.n_kb);
+    };
+    for (int tt = 0; tt < cnt; tt += 2) {
+      step(std::integral_constant<int, 0>(), tt);
+      if (tt + 1 < cnt) step(std::integral_constant<int, 1>(), tt + 1);
     }
   }
 
   // Normalise and store: lane (n, g) holds columns 32cc + 8a + 4g + {0..3} of row qrow.
-  const float lt = l + __shfl_xor(l, 32, 64);
+  const float lt = sum_with_partner(l);
   const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
   if (qrow < p.N) {
     uint16_t* orow = oh + qrow * p.os.n;
