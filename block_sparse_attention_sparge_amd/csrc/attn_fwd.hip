@@ -28,9 +28,12 @@
 //
 // Memory
 //   Q rows stay in registers for the whole walk. K and V tiles go global -> LDS
-//   with global_load_lds_dwordx4 (no registers, no LDS write instructions),
-//   double buffered: tile t+1 is requested before tile t is computed, one
-//   barrier per tile. Tiles are stored unpadded (64 KB of LDS per workgroup at
+//   with buffer_load_dwordx4 ... lds (no data registers, no LDS write
+//   instructions), double buffered with one barrier per tile. The loads of
+//   tile t+1 are interleaved one by one with the QK MFMAs of tile t: issued as
+//   a burst right after the barrier, the loads of all eight wavefronts of a CU
+//   fill the vector-memory queue and stall instruction issue for hundreds of
+//   cycles. Tiles are stored unpadded (64 KB of LDS per workgroup at
 //   D=128, so two workgroups share a CU) with 16-byte chunks XOR-swizzled per
 //   row: K so that the 16 rows one A-operand read touches hit distinct banks,
 //   V so that the 4 rows of one transpose read do.
@@ -52,10 +55,13 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void global_cvoid;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;   // log2 headroom before the running max is raised
+// Word 3 of a raw (untyped) buffer resource on gfx9-family parts.
+constexpr int kBufferFlags = 0x00020000;
+// sched_barrier mask: VALU (0x2), SALU (0x4), LDS reads (0x100), transcendental (0x400).
+constexpr int kSchedKeepLoads = 0x0506;
 
 template <int D>
 struct Cfg {
@@ -201,42 +207,48 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
     voff[cc] = vrow * C::kRowBytes + 16 * ((4 * cc + lcx) ^ vx) + 8 * (lane & 1);
 
   // ---- global -> LDS: wavefront load e fills rows [r0, r0 + kRowsPerInst) of a tile.
-  // Per-lane byte offsets from the tile's first row are fixed; the tile base is scalar.
+  // Loads go through a buffer resource per tile (scalar base and byte bound) with
+  // a fixed 32-bit per-lane offset; rows past N fall outside the bound and read
+  // as zeros (their scores are masked), so ragged and invalid blocks need no
+  // special path.
   uint32_t ld_koff[C::kInstPerWave], ld_voff[C::kInstPerWave];
-  int ld_row[C::kInstPerWave];
 #pragma unroll
   for (int e = 0; e < C::kInstPerWave; ++e) {
     const int inst = wave * C::kInstPerWave + e;
     const int r = inst * C::kRowsPerInst + lane / C::kChunks;
     const int pc = lane % C::kChunks;
-    ld_row[e] = r;
     ld_koff[e] = static_cast<uint32_t>((r * p.ks.n + 8 * (pc ^ swz_k<D>(r))) * 2);
     ld_voff[e] = static_cast<uint32_t>((r * p.vs.n + 8 * (pc ^ swz_v<D>(r))) * 2);
   }
-  // Rows past N (ragged or invalid block) re-read row N-1; their scores are masked.
-  auto issue = [&](int64_t j, const uint16_t* base, int64_t rs, const uint32_t (&off)[C::kInstPerWave],
-                   char* buf) {
-    const char* tb = reinterpret_cast<const char*>(base + j * kKBlock * rs);
-    if (j * kKBlock + kKBlock <= p.N) {
+  auto tile_rsrc = [&](const uint16_t* base, int64_t j, int64_t rs) {
+    int64_t rows = p.N - j * kKBlock;
+    rows = rows < 0 ? 0 : (rows > kKBlock ? kKBlock : rows);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + j * kKBlock * rs), static_cast<short>(0),
+                                             static_cast<int>(rows * rs * 2), kBufferFlags);
+  };
+  auto issue_one = [&](__amdgpu_buffer_rsrc_t rs, uint32_t off, char* buf, int e) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + (wave * C::kInstPerWave + e) * 1024),
+                                             16, static_cast<int>(off), 0, 0, 0);
+  };
+  // Pins a load between the MFMAs around it: VALU, SALU, transcendental and
+  // LDS-read instructions may still move across, MFMAs and memory loads may not.
+  auto pinned_issue = [&](__amdgpu_buffer_rsrc_t rs, uint32_t off, char* buf, int e) {
+    __builtin_amdgcn_sched_barrier(kSchedKeepLoads);
+    issue_one(rs, off, buf, e);
+    __builtin_amdgcn_sched_barrier(kSchedKeepLoads);
+  };
+  auto issue = [&](int64_t j, char* kbuf, char* vbuf) {
+    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kh, j, p.ks.n);
+    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vh, j, p.vs.n);
 #pragma unroll
-      for (int e = 0; e < C::kInstPerWave; ++e)
-        __builtin_amdgcn_global_load_lds((global_cvoid*)(tb + off[e]),
-                                         (lds_void*)(buf + (wave * C::kInstPerWave + e) * 1024),
-                                         16, 0, 0);
-    } else {
-#pragma unroll
-      for (int e = 0; e < C::kInstPerWave; ++e) {
-        const int64_t key = j * kKBlock + ld_row[e];
-        const int64_t back = key < p.N ? 0 : key - (p.N - 1);
-        __builtin_amdgcn_global_load_lds((global_cvoid*)(tb + off[e] - back * rs * 2),
-                                         (lds_void*)(buf + (wave * C::kInstPerWave + e) * 1024),
-                                         16, 0, 0);
-      }
+    for (int e = 0; e < C::kInstPerWave; ++e) {
+      issue_one(kr, ld_koff[e], kbuf, e);
+      issue_one(vr, ld_voff[e], vbuf, e);
     }
   };
 
-  // S^T = K Q^T for keys [0, 32) and [32, 64) of a tile.
-  auto qk = [&](const char* kb, f32x16& s0, f32x16& s1) {
+  // S^T = K Q^T for keys [0, 32) and [32, 64) of a tile; hook(s) runs after k-step s.
+  auto qk = [&](const char* kb, f32x16& s0, f32x16& s1, auto hook) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) { s0[i] = 0.f; s1[i] = 0.f; }
 #pragma unroll
@@ -245,6 +257,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
       const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kb + koff[s] + 32 * C::kRowBytes);
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[s], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[s], s1, 0, 0, 0);
+      hook(s);
     }
   };
 
@@ -328,11 +341,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
     // loads of tile t+1 fill the other pair.
     int64_t j0 = sanitize_id(raw_id(0), p.n_kb);
     int64_t j1 = sanitize_id(raw_id(1), p.n_kb);
-    issue(j0, kh, p.ks.n, ld_koff, lds_k0);
-    issue(j0, vh, p.vs.n, ld_voff, lds_v0);
+    issue(j0, lds_k0, lds_v0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
+    // The next tile's loads are spread through this tile's QK MFMAs, one load
+    // per k-step.
     auto step = [&](auto parity, int tt) {
       constexpr int P = decltype(parity)::value;
       char* k_cur = P ? lds_k1 : lds_k0;
@@ -340,13 +354,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
       char* k_fill = P ? lds_k0 : lds_k1;
       char* v_fill = P ? lds_v0 : lds_v1;
       const bool more = tt + 1 < cnt;
-      if (more) {
-        issue(j1, kh, p.ks.n, ld_koff, k_fill);
-        issue(j1, vh, p.vs.n, ld_voff, v_fill);
-      }
+      // past the last tile the resources hold no bytes: the loads only write
+      // zeros into the buffer that was just released
+      const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kh, more ? j1 : p.n_kb, p.ks.n);
+      const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vh, more ? j1 : p.n_kb, p.vs.n);
       const int32_t raw2 = static_cast<int32_t>(raw_id(tt + 2));
       f32x16 sa, sb;
-      qk(k_cur, sa, sb);
+      qk(k_cur, sa, sb, [&](int st) {
+        // load i of the 2 * kInstPerWave loads (K, then V) follows k-step
+        // i * kSteps / (2 * kInstPerWave): all of tile t+1 is in flight before
+        // the softmax of tile t starts, with PV still ahead to cover its latency
+        constexpr int kLoads = 2 * C::kInstPerWave;
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+          if ((i * C::kSteps) / kLoads == st) {
+            if (i < C::kInstPerWave) pinned_issue(kr, ld_koff[i], k_fill, i);
+            else pinned_issue(vr, ld_voff[i - C::kInstPerWave], v_fill, i - C::kInstPerWave);
+          }
+        }
+      });
       mask_tail(j0, sa, sb);
       const float mref = update_max(sa, sb);
       bf16x8 pb[4];
@@ -365,6 +391,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
       step(std::integral_constant<int, 0>(), tt);
       if (tt + 1 < cnt) step(std::integral_constant<int, 1>(), tt + 1);
     }
+    // no LDS write may still be in flight when the workgroup's LDS is released
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
   // Normalise and store: lane (n, g) holds columns 32cc + 8a + 4g + {0..3} of row qrow.
