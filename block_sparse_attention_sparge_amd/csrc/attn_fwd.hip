@@ -19,12 +19,14 @@
 //   the key order the PV operands need.
 //
 // Softmax
-//   Base 2 with the scale folded into one FMA. The running max is raised only
-//   when a row's tile max exceeds it by more than 2^8 (probabilities then stay
-//   below 256, exact in fp32 and as accurate in bf16), so the output
-//   accumulator is rescaled on a handful of tiles instead of every tile. Row
-//   sums add the bf16-rounded probabilities with v_dot2_f32_bf16, so they match
-//   the weights the PV product actually used.
+//   Base 2 with the scale folded into one FMA. The running max is only a
+//   reference that keeps the weights in range, so no per-tile row max is taken:
+//   weights are computed against the current reference, and only when they
+//   grow too large (their per-lane sum passes 2^20) is the tile's exact max
+//   taken, the reference raised, O and l rescaled and the tile's weights
+//   recomputed; that happens on the first tile of a row and rarely after. Row
+//   sums add the bf16-rounded weights with v_dot2_f32_bf16, so they match the
+//   weights the PV product actually used.
 //
 // Memory
 //   Q rows stay in registers for the whole walk. K and V tiles go global -> LDS
@@ -57,7 +59,8 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRescaleSlack = 8.0f;   // log2 headroom before the running max is raised
+constexpr int kSumLog2 = 20;            // per-lane weight sum that triggers a new reference max
+constexpr float kSumLimit = static_cast<float>(1 << kSumLog2);
 // Word 3 of a raw (untyped) buffer resource on gfx9-family parts.
 constexpr int kBufferFlags = 0x00020000;
 // sched_barrier mask: VALU (0x2), SALU (0x4), LDS reads (0x100), transcendental (0x400).
@@ -151,6 +154,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
 
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // uniform copy for scalar addressing
   const int n = lane & 31, g = lane >> 5;
 
   const uint16_t* qh = p.q + b * p.qs.b + h * p.qs.h;
@@ -227,7 +231,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
                                              static_cast<int>(rows * rs * 2), kBufferFlags);
   };
   auto issue_one = [&](__amdgpu_buffer_rsrc_t rs, uint32_t off, char* buf, int e) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + (wave * C::kInstPerWave + e) * 1024),
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + (wave_s * C::kInstPerWave + e) * 1024),
                                              16, static_cast<int>(off), 0, 0, 0);
   };
   // Pins a load between the MFMAs around it: VALU, SALU, transcendental and
@@ -274,32 +278,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
     }
   };
 
-  // Row max of a tile; raises the running max (and rescales O, l) when the
-  // tile max exceeds it by more than the slack. Returns the max to subtract.
-  auto update_max = [&](const f32x16& s0, const f32x16& s1) -> float {
-    float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-    mx = max_with_partner(mx);
-    const float mt = mx * p.c;
-    if (__builtin_amdgcn_ballot_w64(mt > m + kRescaleSlack)) {
-      const float m_new = fmaxf(m, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);   // 0 on the first tile
-      l *= alpha;
-#pragma unroll
-      for (int cc = 0; cc < C::kDChunks; ++cc)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[cc][i] *= alpha;
-      m = m_new;
-    }
-    // m stays -inf only while every key seen so far was masked (invalid ids);
-    // subtracting 0 then gives zero weights instead of NaN.
-    return (m == -INFINITY) ? 0.f : m;
-  };
-
-  // Probabilities of a tile as bf16 PV operands, and their sum into l.
-  auto probs = [&](const f32x16& s0, const f32x16& s1, float mref, bf16x8 (&pb)[4]) {
+  // Probabilities of a tile as bf16 PV operands, against reference mref (log2
+  // units); returns this lane's sum of the rounded weights.
+  auto probs = [&](const f32x16& s0, const f32x16& s1, float mref, bf16x8 (&pb)[4]) -> float {
     const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    float lt = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
       const f32x2 e0 = {__builtin_amdgcn_exp2f(fmaf(s0[i], p.c, -mref)),
@@ -312,9 +295,42 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
       pb[i >> 3][(i & 7) + 1] = b0[1];
       pb[2 + (i >> 3)][i & 7] = b1[0];
       pb[2 + (i >> 3)][(i & 7) + 1] = b1[1];
-      l = __builtin_amdgcn_fdot2_f32_bf16(b0, ones, l, false);
-      l = __builtin_amdgcn_fdot2_f32_bf16(b1, ones, l, false);
+      lt = __builtin_amdgcn_fdot2_f32_bf16(b0, ones, lt, false);
+      lt = __builtin_amdgcn_fdot2_f32_bf16(b1, ones, lt, false);
     }
+    return lt;
+  };
+
+  // Softmax weights of a tile. The running max m only serves as a reference
+  // that keeps the weights in range, so it is not recomputed per tile: the
+  // weights are taken against the current m, and only when a lane's weights
+  // sum past 2^kSumLog2 (a score far above m; or m still unset) is the tile's
+  // exact row max taken, m raised to it, O and l rescaled, and the weights
+  // recomputed. Weights up to 2^kSumLog2 are as exact in bf16 and fp32 as
+  // weights below 1, and the accumulators have ample range for them.
+  auto weights = [&](const f32x16& s0, const f32x16& s1, bf16x8 (&pb)[4]) {
+    // m stays -inf only while every key seen so far was masked (invalid ids);
+    // a reference of 0 then gives zero weights instead of NaN.
+    float mref = (m == -INFINITY) ? 0.f : m;
+    float lt = probs(s0, s1, mref, pb);
+    if (__builtin_amdgcn_ballot_w64(!(lt <= kSumLimit) || (m == -INFINITY && lt > 0.f))) {
+      float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+      const float mt = max_with_partner(mx) * p.c;
+      const float m_new = fmaxf(m, mt);
+      // O and l are still 0 while m is unset
+      const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int cc = 0; cc < C::kDChunks; ++cc)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[cc][i] *= alpha;
+      m = m_new;
+      mref = (m == -INFINITY) ? 0.f : m;
+      lt = probs(s0, s1, mref, pb);
+    }
+    l += lt;
   };
 
   // O^T += V^T P^T over four 16-key steps.
@@ -374,9 +390,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
         }
       });
       mask_tail(j0, sa, sb);
-      const float mref = update_max(sa, sb);
       bf16x8 pb[4];
-      probs(sa, sb, mref, pb);
+      weights(sa, sb, pb);
       pv(v_cur, pb);
       j0 = j1;
       j1 = sanitize_id(raw2, p.n_kb);

@@ -154,6 +154,29 @@ def test_strided_layouts_and_scale(gpu_lib):
     assert_close(to_host_f64(a), ref, "scale=0.05")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("pattern", ["growing", "shrinking", "wide"])
+def test_softmax_reference_raised(gpu_lib, D, pattern):
+    """Scores that climb far above the running max along the key walk (and the
+    reverse, and a very wide spread) exercise the rescaling of O and l."""
+    B, H, N = 1, 2, 1000
+    q, k, v = rand_qkv(B, H, N, D, seed=41 + D)
+    kf = F64(k)
+    blk = np.arange(N) // 64
+    if pattern == "growing":
+        kf = kf * (1.0 + 1.5 * blk)[None, None, :, None]
+    elif pattern == "shrinking":
+        kf = kf * (1.0 + 1.5 * (blk.max() - blk))[None, None, :, None]
+    else:
+        kf = kf * 6.0
+    kb = synth.f32_to_bf16_bits(kf.astype(np.float32))
+    scale = 1.0 if pattern == "wide" else None
+    out = sp.block_sparse_attn(*_dev(q, kb, v), mask_id=None, scale=scale)
+    mask = np.ones(sp.mask_shape(B, H, N), dtype=np.uint8)
+    ref = oracle.masked_attention(F64(q), F64(kb), F64(v), mask, scale=scale)
+    print(assert_close(to_host_f64(out), ref, f"{pattern} D={D}"))
+
+
 def test_deterministic(gpu_lib):
     wl = synth.WORKLOADS[0]
     q, k, v = synth.make_qkv(wl)
