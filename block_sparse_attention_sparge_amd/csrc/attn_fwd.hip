@@ -268,10 +268,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   // Keys past N in a ragged (or invalid) block take no weight.
   auto mask_tail = [&](int64_t j, f32x16& s0, f32x16& s1) {
     if (j * kKBlock + kKBlock > p.N) {
-      const int64_t lim = p.N - j * kKBlock;
+      // register i of this lane holds key 8g + i (i < 8) or 8g + 16 + (i - 8);
+      // keys from lim on are masked
+      const int64_t lim64 = p.N - j * kKBlock;
+      const int lim = static_cast<int>(lim64 < 0 ? 0 : lim64) - 8 * g;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int kl = (i < 8) ? 8 * g + i : 16 + 8 * g + (i - 8);
+        const int kl = (i < 8) ? i : 16 + (i - 8);
         if (kl >= lim) s0[i] = -INFINITY;
         if (kl + 32 >= lim) s1[i] = -INFINITY;
       }
