@@ -27,6 +27,14 @@ What it computes, in the order of the method:
    tokens that don't meaningfully interact" idea of the Apply SpargeAttn page,
    opening section.
 
+Causal variant (the API's is_causal flag, same paragraph; the pages give no
+more): key c is visible to query row r when c <= r. Query block i may only
+select the key blocks holding a key visible to one of its rows, j <= J(i) =
+floor((last row of block i) / 64); it keeps ceil(topk * (J(i) + 1)) of them
+(same rounding rule), ranked as above over those candidates only, and inside
+the kept blocks each row attends to its visible keys only. A row left with no
+visible kept key outputs zeros.
+
 Steps 1-3 are this build's plain reading of the API name meansim_topk: block
 means, a similarity between them, top-k. The pages name the method but do not
 spell it out. Step 4 is an exact mathematical result; any correct
@@ -113,21 +121,46 @@ def select_topk(p: np.ndarray, k: int) -> np.ndarray:
     return mask.reshape(p.shape)
 
 
-def predict_mask(q: np.ndarray, k: np.ndarray, topk: float, scale: float | None = None) -> dict:
+def causal_key_blocks(n: int, i: int) -> int:
+    """Key blocks 0 .. J(i) hold a key that some row of query block i may see
+    under causal masking (key c visible to row r when c <= r); returns J(i) + 1,
+    with J(i) = floor(last row of block i / 64)."""
+    last_row = min(n, (i + 1) * Q_BLOCK) - 1
+    return last_row // K_BLOCK + 1
+
+
+def predict_mask(q: np.ndarray, k: np.ndarray, topk: float, scale: float | None = None,
+                 causal: bool = False) -> dict:
     """Pool -> score -> select. q, k are (B, H, N, D) float64.
 
     Returns a dict with mask (uint8), logits s, probabilities p, the pooled
-    qbar / kbar and the per-row count kk.
+    qbar / kbar, the count k (an int, or with causal=True a per-query-block
+    array) and the number of candidate key blocks per query block ("cand").
+    With causal=True the softmax and the selection of query block i run over
+    key blocks 0 .. J(i) only (see causal_key_blocks) and keep
+    topk_count(J(i) + 1, topk) of them; the other entries of the row are 0.
     """
-    d = q.shape[-1]
+    n, d = q.shape[-2], q.shape[-1]
     scale = default_scale(d) if scale is None else float(scale)
     qbar = pool_blocks(q, Q_BLOCK)
     kbar = pool_blocks(k, K_BLOCK)
     s = block_logits(qbar, kbar, scale)
-    p = row_softmax(s)
-    kk = topk_count(kbar.shape[-2], topk)
-    mask = select_topk(p, kk)
-    return {"mask": mask, "logits": s, "probs": p, "qbar": qbar, "kbar": kbar, "k": kk}
+    n_qb, n_kb = qbar.shape[-2], kbar.shape[-2]
+    if not causal:
+        p = row_softmax(s)
+        kk = topk_count(n_kb, topk)
+        mask = select_topk(p, kk)
+        return {"mask": mask, "logits": s, "probs": p, "qbar": qbar, "kbar": kbar, "k": kk,
+                "cand": np.full(n_qb, n_kb, dtype=np.int64)}
+    cand = np.array([causal_key_blocks(n, i) for i in range(n_qb)], dtype=np.int64)
+    kk = np.array([topk_count(int(c), topk) for c in cand], dtype=np.int64)
+    p = np.zeros_like(s)
+    mask = np.zeros(s.shape, dtype=np.uint8)
+    for i in range(n_qb):
+        c = int(cand[i])
+        p[..., i, :c] = row_softmax(s[..., i, :c])
+        mask[..., i, :c] = select_topk(p[..., i, :c], int(kk[i]))
+    return {"mask": mask, "logits": s, "probs": p, "qbar": qbar, "kbar": kbar, "k": kk, "cand": cand}
 
 
 def selected_keys(mask_row: np.ndarray, n: int) -> np.ndarray:
@@ -138,19 +171,33 @@ def selected_keys(mask_row: np.ndarray, n: int) -> np.ndarray:
     return np.asarray(idx, dtype=np.int64)
 
 
-def attend_rows(q_rows: np.ndarray, k_sel: np.ndarray, v_sel: np.ndarray, scale: float) -> np.ndarray:
-    """Softmax attention of some query rows over one key/value set (float64)."""
+def attend_rows(q_rows: np.ndarray, k_sel: np.ndarray, v_sel: np.ndarray, scale: float,
+                row_ids: np.ndarray | None = None, col_ids: np.ndarray | None = None) -> np.ndarray:
+    """Softmax attention of some query rows over one key/value set (float64).
+
+    With row_ids / col_ids (token indices of the rows and of the keys) the
+    attention is causal: row r only weighs keys c <= r; a row that sees no key
+    outputs zeros.
+    """
+    out = np.zeros((q_rows.shape[0], v_sel.shape[-1]), dtype=np.float64)
     if k_sel.shape[0] == 0:
-        return np.zeros((q_rows.shape[0], v_sel.shape[-1]), dtype=np.float64)
+        return out
     logits = float(scale) * (q_rows @ k_sel.T)
-    w = row_softmax(logits)
-    return w @ v_sel
+    if row_ids is None:
+        return row_softmax(logits) @ v_sel
+    visible = np.asarray(col_ids)[None, :] <= np.asarray(row_ids)[:, None]
+    for r in range(q_rows.shape[0]):
+        cols = np.flatnonzero(visible[r])
+        if cols.size:
+            out[r] = row_softmax(logits[r, cols]) @ v_sel[cols]
+    return out
 
 
-def masked_attention(q, k, v, mask, scale: float | None = None) -> np.ndarray:
-    """Block-masked non-causal attention; q, k, v (B, H, N, D) float64, mask (B, H, Qb, Kb).
+def masked_attention(q, k, v, mask, scale: float | None = None, causal: bool = False) -> np.ndarray:
+    """Block-masked attention; q, k, v (B, H, N, D) float64, mask (B, H, Qb, Kb).
 
-    A query block with no selected key block outputs zeros.
+    A query block with no selected key block outputs zeros. With causal=True a
+    row r only sees the keys c <= r of its selected blocks (zeros if none).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -166,11 +213,14 @@ def masked_attention(q, k, v, mask, scale: float | None = None) -> np.ndarray:
             for i in range(qb):
                 lo, hi = i * Q_BLOCK, min(N, (i + 1) * Q_BLOCK)
                 cols = selected_keys(mask[b, h, i], N)
-                out[b, h, lo:hi] = attend_rows(q[b, h, lo:hi], k[b, h, cols], v[b, h, cols], scale)
+                rows = np.arange(lo, hi) if causal else None
+                out[b, h, lo:hi] = attend_rows(q[b, h, lo:hi], k[b, h, cols], v[b, h, cols], scale,
+                                               rows, cols if causal else None)
     return out
 
 
-def masked_attention_rows(q_h, k_h, v_h, mask_h, rows, scale: float | None = None) -> np.ndarray:
+def masked_attention_rows(q_h, k_h, v_h, mask_h, rows, scale: float | None = None,
+                          causal: bool = False) -> np.ndarray:
     """Outputs of chosen query rows of one head; q_h, k_h, v_h (N, D), mask_h (Qb, Kb)."""
     q_h = np.asarray(q_h, dtype=np.float64)
     N, D = q_h.shape
@@ -182,7 +232,8 @@ def masked_attention_rows(q_h, k_h, v_h, mask_h, rows, scale: float | None = Non
         sel = np.flatnonzero(blocks == i)
         cols = selected_keys(mask_h[i], N)
         out[sel] = attend_rows(q_h[rows[sel]], np.asarray(k_h, dtype=np.float64)[cols],
-                               np.asarray(v_h, dtype=np.float64)[cols], scale)
+                               np.asarray(v_h, dtype=np.float64)[cols], scale,
+                               rows[sel] if causal else None, cols if causal else None)
     return out
 
 
@@ -203,31 +254,44 @@ def compact_mask(mask: np.ndarray):
     return idx.reshape(mask.shape), cnt.reshape(mask.shape[:-1])
 
 
-def mask_parity(logits: np.ndarray, oracle_mask: np.ndarray, device_mask: np.ndarray, k: int,
-                band: float = 1e-5, probs: np.ndarray | None = None) -> dict:
+def mask_parity(logits: np.ndarray, oracle_mask: np.ndarray, device_mask: np.ndarray, k,
+                band: float = 1e-5, probs: np.ndarray | None = None, cand=None) -> dict:
     """Compare a device mask with the oracle's, allowing near-ties at the top-k boundary.
 
-    Per row, with the row's logits sorted in decreasing order, t is the k-th
-    largest and the gap is t minus the (k+1)-th largest (infinite when k is
-    the row length). A row whose gap is at least `band` must equal the oracle
-    row exactly. A row whose gap is below `band` is an exception candidate: it
-    passes when it keeps exactly k blocks, keeps every block whose logit is
-    at least t + band and drops every block whose logit is at most t - band.
+    Per row, with the row's candidate logits sorted in decreasing order, t is
+    the k-th largest and the gap is t minus the (k+1)-th largest (infinite
+    when k is the number of candidates). A row whose gap is at least `band`
+    must equal the oracle row exactly. A row whose gap is below `band` is an
+    exception candidate: it passes when it keeps exactly k blocks, keeps every
+    block whose logit is at least t + band and drops every block whose logit
+    is at most t - band. k and cand (candidates per row, default all key
+    blocks) may be ints or per-query-block arrays; blocks past a row's
+    candidates must never be kept.
     """
     s = np.asarray(logits, dtype=np.float64).reshape(-1, logits.shape[-1])
     om = np.asarray(oracle_mask).reshape(s.shape) != 0
     dm = np.asarray(device_mask).reshape(s.shape) != 0
     R, kb = s.shape
-    srt = -np.sort(-s, axis=1)
-    t = srt[:, k - 1]
-    gap = t - srt[:, k] if k < kb else np.full(R, np.inf)
+    n_qb = logits.shape[-2]
+    kr = np.broadcast_to(np.asarray(k, dtype=np.int64), (n_qb,))
+    cr = np.broadcast_to(np.asarray(kb if cand is None else cand, dtype=np.int64), (n_qb,))
+    kr = np.tile(kr, R // n_qb)
+    cr = np.tile(cr, R // n_qb)
+    in_cand = np.arange(kb)[None, :] < cr[:, None]
+    sc = np.where(in_cand, s, -np.inf)
+    srt = -np.sort(-sc, axis=1)
+    rows = np.arange(R)
+    t = srt[rows, kr - 1]
+    nxt = srt[rows, np.minimum(kr, kb - 1)]
+    gap = np.where(kr < cr, t - nxt, np.inf)
     near = gap < band
     differ = (om != dm).any(axis=1)
     ok_exact = ~differ
-    count_ok = dm.sum(axis=1) == k
-    must_keep = s >= (t + band)[:, None]
-    must_drop = s <= (t - band)[:, None]
-    ok_near = count_ok & ~(must_keep & ~dm).any(axis=1) & ~(must_drop & dm).any(axis=1)
+    count_ok = dm.sum(axis=1) == kr
+    outside_ok = ~(dm & ~in_cand).any(axis=1)
+    must_keep = in_cand & (s >= (t + band)[:, None])
+    must_drop = in_cand & (s <= (t - band)[:, None])
+    ok_near = count_ok & outside_ok & ~(must_keep & ~dm).any(axis=1) & ~(must_drop & dm).any(axis=1)
     ok = np.where(near, ok_near, ok_exact)
     rep = {
         "rows": int(R),
@@ -237,7 +301,7 @@ def mask_parity(logits: np.ndarray, oracle_mask: np.ndarray, device_mask: np.nda
         "failing_rows": np.flatnonzero(~ok)[:16].tolist(),
     }
     if probs is not None:
-        ps = -np.sort(-np.asarray(probs, dtype=np.float64).reshape(s.shape), axis=1)
-        pgap = ps[:, k - 1] - ps[:, k] if k < kb else np.full(R, np.inf)
+        ps = -np.sort(-np.where(in_cand, np.asarray(probs, dtype=np.float64).reshape(s.shape), -np.inf), axis=1)
+        pgap = np.where(kr < cr, ps[rows, kr - 1] - ps[rows, np.minimum(kr, kb - 1)], np.inf)
         rep["prob_domain_candidates"] = int((pgap < band).sum())
     return rep

@@ -23,7 +23,8 @@ GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 def _ns(**over):
     names = ["Q_BLOCK", "K_BLOCK", "num_blocks", "default_scale", "topk_count", "pool_blocks",
              "block_logits", "row_softmax", "select_topk", "predict_mask", "selected_keys",
-             "attend_rows", "masked_attention", "masked_attention_rows", "compact_mask", "mask_parity"]
+             "attend_rows", "masked_attention", "masked_attention_rows", "compact_mask", "mask_parity",
+             "causal_key_blocks"]
     d = {n: getattr(real_oracle, n) for n in names}
     d.update(over)
     return types.SimpleNamespace(**d)
@@ -39,12 +40,12 @@ def _golden(name):
     return rows
 
 
-def _sdpa(q, k, v, scale, bool_mask=None):
+def _sdpa(q, k, v, scale, bool_mask=None, is_causal=False):
     """torch's scaled_dot_product_attention in float64 on the CPU."""
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a))
     m = None if bool_mask is None else torch.from_numpy(bool_mask)
     return torch.nn.functional.scaled_dot_product_attention(
-        t(q), t(k), t(v), attn_mask=m, scale=scale).numpy()
+        t(q), t(k), t(v), attn_mask=m, scale=scale, is_causal=is_causal).numpy()
 
 
 def _expand(mask, n):
@@ -286,9 +287,88 @@ def pin_mask_parity(o):
     assert o.mask_parity(s, om, dm, 2)["failures"] == 1
 
 
+def pin_causal_attention(o):
+    rng = np.random.default_rng(10)
+    for n, d in ((200, 8), (131, 4), (256, 16)):
+        q, k, v = (rng.standard_normal((1, 2, n, d)) for _ in range(3))
+        qb, kb = -(-n // 128), -(-n // 64)
+        sc = 1.0 / math.sqrt(d)
+        tril = np.tril(np.ones((n, n), dtype=bool))
+        # all blocks kept: torch's causal SDPA
+        ones = np.ones((1, 2, qb, kb), dtype=np.uint8)
+        ref = _sdpa(q, k, v, sc, is_causal=True)
+        assert np.abs(o.masked_attention(q, k, v, ones, causal=True) - ref).max() <= 1e-12
+        # a random block mask that keeps block 0 (key 0 is visible to every row)
+        m = (rng.random((1, 2, qb, kb)) < 0.5).astype(np.uint8)
+        m[..., :, 0] = 1
+        got = o.masked_attention(q, k, v, m, causal=True)
+        assert np.abs(got - _sdpa(q, k, v, sc, _expand(m, n) & tril)).max() <= 1e-12
+        # brute force on a few rows
+        for row in (0, 63, 64, n - 1):
+            i = row // 128
+            cols = [c for c in range(n) if m[0, 1, i, c // 64] and c <= row]
+            lg = [sc * sum(q[0, 1, row, t] * k[0, 1, c, t] for t in range(d)) for c in cols]
+            mx = max(lg)
+            w = [math.exp(x - mx) for x in lg]
+            z = sum(w)
+            for t in range(d):
+                assert abs(got[0, 1, row, t] - sum(wi * v[0, 1, c, t] for wi, c in zip(w, cols)) / z) <= 1e-12
+        # rows that see no kept key output zeros; the rest follow the masked SDPA
+        late = np.zeros_like(m)
+        late[..., :, kb - 1] = 1
+        out = o.masked_attention(q, k, v, late, causal=True)
+        first = 64 * (kb - 1)
+        assert (out[..., :first, :] == 0).all()
+        ref = _sdpa(q[..., first:, :], k[..., first:, :], v[..., first:, :], sc, is_causal=True)
+        assert np.abs(out[..., first:, :] - ref).max() <= 1e-12
+        # the row-sampled form agrees
+        rows = np.array([0, 1, 64, n - 1])
+        assert np.abs(o.masked_attention_rows(q[0, 0], k[0, 0], v[0, 0], m[0, 0], rows, causal=True)
+                      - got[0, 0][rows]).max() <= 1e-12
+
+
+def pin_causal_predict(o):
+    # candidate blocks: brute force over (row, key) pairs
+    for n in (1, 63, 64, 65, 128, 129, 200, 256, 300, 1000):
+        qb, kb = -(-n // 128), -(-n // 64)
+        for i in range(qb):
+            seen = set()
+            for r in range(128 * i, min(n, 128 * i + 128)):
+                for c in range(0, r + 1):
+                    seen.add(c // 64)
+            assert o.causal_key_blocks(n, i) == len(seen) == max(seen) + 1
+    rng = np.random.default_rng(11)
+    n, d = 700, 8
+    q, k = rng.standard_normal((1, 2, n, d)), rng.standard_normal((1, 2, n, d))
+    qb, kb = -(-n // 128), -(-n // 64)
+    full = o.predict_mask(q, k, 1.0, causal=True)
+    for i in range(qb):
+        c = 2 * i + 2 if 128 * i + 127 < n else kb
+        assert full["mask"][..., i, :c].all() and not full["mask"][..., i, c:].any()
+    for topk in (0.3, 0.55):
+        r = o.predict_mask(q, k, topk, causal=True)
+        s = np.einsum("bhid,bhjd->bhij", o.pool_blocks(q, 128), o.pool_blocks(k, 64)) / math.sqrt(d)
+        for i in range(qb):
+            c = o.causal_key_blocks(n, i)
+            kk = max(1, min(c, math.ceil(topk * c - 1e-9)))
+            assert int(r["k"][i]) == kk
+            for h in range(2):
+                order = sorted(range(c), key=lambda j: (-s[0, h, i, j], j))[:kk]
+                assert sorted(np.flatnonzero(r["mask"][0, h, i]).tolist()) == sorted(order)
+    # parity: a device row keeping a block outside its candidates fails
+    r = o.predict_mask(q, k, 0.3, causal=True)
+    dm = r["mask"].copy()
+    dm[0, 0, 0, :] = 0
+    dm[0, 0, 0, kb - 1] = 1
+    dm[0, 0, 0, 0] = 1
+    rep = o.mask_parity(r["logits"], r["mask"], dm, r["k"], cand=r["cand"])
+    assert rep["failures"] >= 1
+    assert o.mask_parity(r["logits"], r["mask"], r["mask"], r["k"], cand=r["cand"])["failures"] == 0
+
+
 PINS = [pin_block_counts, pin_topk_count, pin_pool, pin_scores, pin_select, pin_predict,
         pin_predict_ties, pin_attention, pin_attention_closed_forms, pin_attention_rows,
-        pin_compact, pin_mask_parity]
+        pin_compact, pin_mask_parity, pin_causal_attention, pin_causal_predict]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -338,13 +418,15 @@ def _broken_variants():
             raise ValueError
         return max(1, min(kb, math.ceil(topk * kb)))
 
-    def attend_no_scale(qr, ks, vs, scale):
-        return o.attend_rows(qr, ks, vs, 1.0)
+    def attend_no_scale(qr, ks, vs, scale, rows=None, cols=None):
+        return o.attend_rows(qr, ks, vs, 1.0, rows, cols)
 
-    def attend_unnormalised(qr, ks, vs, scale):
+    def attend_unnormalised(qr, ks, vs, scale, rows=None, cols=None):
         if ks.shape[0] == 0:
             return np.zeros((qr.shape[0], vs.shape[-1]))
         lg = scale * (qr @ ks.T)
+        if rows is not None:
+            lg = np.where(np.asarray(cols)[None, :] <= np.asarray(rows)[:, None], lg, -np.inf)
         return np.exp(lg - lg.max(-1, keepdims=True)) @ vs
 
     def selected_keys_wrong_block(mask_row, n):
@@ -360,14 +442,28 @@ def _broken_variants():
                 idx.extend(range(j * 64, (j + 1) * 64))
         return np.asarray(idx, dtype=np.int64)
 
-    def attend_transposed_v(qr, ks, vs, scale):
-        if ks.shape[0] == 0:
-            return np.zeros((qr.shape[0], vs.shape[-1]))
-        w = o.row_softmax(scale * (qr @ ks.T))
-        return (w @ ks)            # uses K where V belongs
+    def attend_transposed_v(qr, ks, vs, scale, rows=None, cols=None):
+        return o.attend_rows(qr, ks, ks, scale, rows, cols)   # uses K where V belongs
 
-    def parity_no_band(logits, om, dm, k, band=1e-5, probs=None):
-        return o.mask_parity(logits, om, dm, k, band=0.0, probs=probs)
+    def attend_causal_strict(qr, ks, vs, scale, rows=None, cols=None):
+        if rows is None:
+            return o.attend_rows(qr, ks, vs, scale)
+        out = np.zeros((qr.shape[0], vs.shape[-1]))
+        lg = scale * (qr @ ks.T)
+        for r in range(qr.shape[0]):
+            c = np.flatnonzero(np.asarray(cols) < rows[r])      # a row does not see its own key
+            if c.size:
+                out[r] = o.row_softmax(lg[r, c]) @ vs[c]
+        return out
+
+    def causal_first_row(n, i):
+        return (128 * i) // 64 + 1
+
+    def causal_all_blocks(n, i):
+        return -(-n // 64)
+
+    def parity_no_band(logits, om, dm, k, band=1e-5, probs=None, cand=None):
+        return o.mask_parity(logits, om, dm, k, band=0.0, probs=probs, cand=cand)
 
     return {
         "pool divides by the full block size": dict(pool_blocks=pool_full_divisor),
@@ -383,6 +479,9 @@ def _broken_variants():
         "ragged last key block dropped": dict(selected_keys=selected_keys_drop_tail),
         "K used in place of V": dict(attend_rows=attend_transposed_v),
         "parity without the near-tie band": dict(mask_parity=parity_no_band),
+        "causal row does not see its own key": dict(attend_rows=attend_causal_strict),
+        "causal candidates from the block's first row": dict(causal_key_blocks=causal_first_row),
+        "causal candidates include future blocks": dict(causal_key_blocks=causal_all_blocks),
     }, src
 
 
