@@ -51,6 +51,7 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--causal", action="store_true", help="causal variant (is_causal=True)")
     p.add_argument("--kernels-only", action="store_true",
                    help="launch each kernel once plus a plain copy of known size, for counter runs")
     return p.parse_args()
@@ -66,12 +67,26 @@ def block_rows_cols(N: int):
     return rows, cols
 
 
-def effective_flops(mask: np.ndarray, N: int, D: int) -> float:
-    """4*D * sum over kept tiles of (valid query rows) x (valid keys); mask (..., Qb, Kb)."""
+def tile_pairs(N: int, causal: bool) -> np.ndarray:
+    """(Qb, Kb) number of (query row, key) pairs a tile computes: valid rows x valid keys,
+    and with causal masking only the pairs with key <= row."""
     rows, cols = block_rows_cols(N)
+    if not causal:
+        return np.outer(rows, cols)
+    qb, kb = rows.size, cols.size
+    k0 = 64.0 * np.arange(kb)
+    out = np.empty((qb, kb))
+    for i in range(qb):
+        r = np.arange(128 * i, 128 * i + int(rows[i]), dtype=np.float64)
+        out[i] = np.clip(r[:, None] + 1.0 - k0[None, :], 0.0, cols[None, :]).sum(0)
+    return out
+
+
+def effective_flops(mask: np.ndarray, N: int, D: int, causal: bool = False) -> float:
+    """4*D * sum over kept tiles of the (query row, key) pairs they compute; mask (..., Qb, Kb)."""
     qb, kb = mask.shape[-2:]
-    per_row = mask.reshape(-1, qb, kb).astype(np.float64) @ cols        # (BH, qb)
-    return 4.0 * D * float((per_row @ rows).sum())
+    pairs = tile_pairs(N, causal)
+    return 4.0 * D * float((mask.reshape(-1, qb, kb).astype(np.float64) * pairs[None]).sum())
 
 
 def kernel_durations_ms(fn, iters):
@@ -92,19 +107,20 @@ def source_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def load_traffic(per_launch_flops):
-    """HBM bytes per attention launch from the committed rocprofv3 counter runs, if still current."""
+def load_traffic(workload: str):
+    """HBM bytes per attention launch from the committed rocprofv3 counter runs, if they
+    were taken on this workload and the attention source has not changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("attn_fwd_source_sha256_16") != source_hash(ATTN_SOURCE):
+    if t.get("attn_fwd_source_sha256_16") != source_hash(ATTN_SOURCE) or t.get("workload") != workload:
         return None
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, q, k, v, topk, budget_s):
+def cpu_baseline(wl, q, k, v, topk, budget_s, causal=False):
     """The fp64 oracle on the host cores: head 0's full prediction plus attention for as
     many of its query blocks as fit in the time budget (in block order)."""
     import oracle
@@ -122,19 +138,19 @@ def cpu_baseline(wl, q, k, v, topk, budget_s):
         f64 = synth.bf16_bits_to_f64
         qh, kh, vh = f64(q[0, 0]), f64(k[0, 0]), f64(v[0, 0])
         t0 = time.perf_counter()
-        pr = oracle.predict_mask(qh[None, None], kh[None, None], topk)
+        pr = oracle.predict_mask(qh[None, None], kh[None, None], topk, causal=causal)
         t_pred = time.perf_counter() - t0
         m = pr["mask"][0, 0]
         qb = m.shape[0]
         done, t_attn, flops = 0, 0.0, 0.0
         N, D = qh.shape
+        pairs = tile_pairs(N, causal)
         while done < qb and (done < 4 or t_pred + t_attn < budget_s):
             rows = np.arange(128 * done, min(N, 128 * done + 128))
             t1 = time.perf_counter()
-            oracle.masked_attention_rows(qh, kh, vh, m, rows)
+            oracle.masked_attention_rows(qh, kh, vh, m, rows, causal=causal)
             t_attn += time.perf_counter() - t1
-            brows, bcols = block_rows_cols(N)
-            flops += 4.0 * D * brows[done] * float(m[done].astype(np.float64) @ bcols)
+            flops += 4.0 * D * float(m[done].astype(np.float64) @ pairs[done])
             done += 1
         bh = wl.B * wl.H
         full_attn_s = t_attn * (qb / done) * bh
@@ -182,18 +198,20 @@ def main():
     ws = torch.empty(sp.workspace_bytes(B, H, N, D, topk), dtype=torch.uint8, device=dev)
     kk = sp.topk_count(mask.shape[-1], topk)
 
+    causal = bool(args.causal)
+
     def step():
-        sp.attn_topk(dq, dk, dv, topk=topk, out=out, workspace=ws)
+        sp.attn_topk(dq, dk, dv, topk=topk, out=out, workspace=ws, is_causal=causal)
 
     # mask and lists once, for the per-kernel timings and the flop count
-    sp.attn_topk(dq, dk, dv, topk=topk, out=out, workspace=ws)
+    step()
     torch.cuda.synchronize()
     qbar, kbar = sp.pool_blocks(dq, 128), sp.pool_blocks(dk, 64)
-    mask_t, idx, cnt = sp.predict_mask(qbar, kbar, N, topk)
+    mask_t, idx, cnt = sp.predict_mask(qbar, kbar, N, topk, is_causal=causal)
     torch.cuda.synchronize()
     m = mask_t.cpu().numpy()
-    eff = effective_flops(m, N, D)
-    dense = 4.0 * B * H * N * N * D
+    eff = effective_flops(m, N, D, causal)
+    dense = 4.0 * B * H * D * (N * (N + 1) / 2.0 if causal else float(N) * N)
     log(f"k={kk} of {m.shape[-1]} key blocks; effective {eff / 1e12:.2f} TFLOP, dense {dense / 1e12:.2f} TFLOP")
 
     if args.kernels_only:
@@ -202,10 +220,10 @@ def main():
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        sp.attn_from_list(dq, dk, dv, idx, cnt, out=out)
+        sp.attn_from_list(dq, dk, dv, idx, cnt, out=out, is_causal=causal)
         sp.pool_blocks(dq, 128)
         sp.pool_blocks(dk, 64)
-        sp.predict_mask(qbar, kbar, N, topk)
+        sp.predict_mask(qbar, kbar, N, topk, is_causal=causal)
         dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"kernels_only": True, "copy_bytes": COPY_BYTES, "workload": wl.name,
@@ -228,13 +246,16 @@ def main():
 
     # attention kernel alone, launch by launch
     attn_iters = max(5, min(args.steps, 20))
-    attn = kernel_durations_ms(lambda: sp.attn_from_list(dq, dk, dv, idx, cnt, out=out), attn_iters)
+    attn = kernel_durations_ms(lambda: sp.attn_from_list(dq, dk, dv, idx, cnt, out=out, is_causal=causal),
+                               attn_iters)
     attn_ms = float(np.mean(attn))
     log(f"attention kernel {attn_ms:.3f} ms (min {min(attn):.3f})")
     pool_q = kernel_durations_ms(lambda: sp.pool_blocks(dq, 128), 10)
     pool_k = kernel_durations_ms(lambda: sp.pool_blocks(dk, 64), 10)
-    pred = kernel_durations_ms(lambda: sp.predict_mask(qbar, kbar, N, topk, return_mask=True), 10)
-    bsa = kernel_durations_ms(lambda: sp.block_sparse_attn(dq, dk, dv, mask_id=mask_t, out=out), 5)
+    pred = kernel_durations_ms(lambda: sp.predict_mask(qbar, kbar, N, topk, return_mask=True,
+                                                       is_causal=causal), 10)
+    bsa = kernel_durations_ms(lambda: sp.block_sparse_attn(dq, dk, dv, mask_id=mask_t, out=out,
+                                                           is_causal=causal), 5)
 
     qb_, kb_ = m.shape[-2:]
     pool_bytes_q = B * H * N * D * 2 + B * H * qb_ * D * 4
@@ -256,6 +277,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "H": H, "N": N, "D": D, "topk": topk, "k": kk,
+                   "causal": causal,
                    "n_qblocks": int(qb_), "n_kblocks": int(kb_), "seed": args.seed,
                    "step": "sparge_attn_topk (pool Q, pool K, predict, attention)"},
         "dense_equiv_tflops": dense / (ms * 1e-3) / 1e12,
@@ -273,12 +295,12 @@ def main():
                     "gbs": pred_bytes / (np.mean(pred) * 1e-3) / 1e9},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": load_traffic(eff),
-                     "kernel": "attn_fwd_kernel<128> (sparge_attn_from_list)"},
+                     "traffic": None if causal else load_traffic(f"{wl.name}_topk{topk}"),
+                     "kernel": f"attn_fwd_kernel<{D}> (sparge_attn_from_list)"},
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle sample")
-        result["cpu_baseline"] = cpu_baseline(wl, q, k, v, topk, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(wl, q, k, v, topk, args.cpu_seconds, causal)
     print(json.dumps(result), flush=True)
 
 

@@ -74,14 +74,14 @@ def load_library() -> ctypes.CDLL:
         "sparge_topk_count": (ci, [i64, f64, ctypes.POINTER(ctypes.c_int64)]),
         "sparge_workspace_bytes": (sz, [i64, i64, i64, i64, f64]),
         "sparge_pool_blocks": (ci, [vp, i64, i64, i64, i64, s3, ci, vp, vp]),
-        "sparge_predict_mask": (ci, [vp, vp, i64, i64, i64, i64, f64, f32, vp, vp, vp, vp]),
+        "sparge_predict_mask": (ci, [vp, vp, i64, i64, i64, i64, f64, f32, ci, vp, vp, vp, vp]),
         "sparge_compact_mask": (ci, [vp, i64, i64, i64, vp, vp, vp]),
         "sparge_attn_from_list": (ci, [vp, vp, vp, vp, vp, i64, vp, i64, i64, i64, i64,
-                                       s3, s3, s3, s3, f32, vp]),
+                                       s3, s3, s3, s3, f32, ci, vp]),
         "block_sparse_attn": (ci, [vp, vp, vp, vp, vp, i64, i64, i64, i64, s3, s3, s3, s3, f32,
-                                   vp, sz, vp]),
+                                   ci, vp, sz, vp]),
         "sparge_attn_topk": (ci, [vp, vp, vp, f64, vp, i64, i64, i64, i64, s3, s3, s3, s3, f32,
-                                  vp, vp, sz, vp]),
+                                  ci, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -188,8 +188,12 @@ def pool_blocks(x: torch.Tensor, block_rows: int) -> torch.Tensor:
 
 
 def predict_mask(qbar: torch.Tensor, kbar: torch.Tensor, N: int, topk: float, scale=None,
-                 return_mask: bool = True):
-    """Top-k block selection from pooled means. Returns (mask_id or None, kv_idx, kv_cnt)."""
+                 return_mask: bool = True, is_causal: bool = False):
+    """Top-k block selection from pooled means. Returns (mask_id or None, kv_idx, kv_cnt).
+
+    With is_causal=True, query block i ranks only the key blocks holding a key
+    one of its rows may see and keeps the top-k share of those (kv_cnt per row).
+    """
     if qbar.dtype != torch.float32 or kbar.dtype != torch.float32:
         raise ValueError("qbar and kbar must be float32")
     qbar, kbar = qbar.contiguous(), kbar.contiguous()
@@ -203,8 +207,8 @@ def predict_mask(qbar: torch.Tensor, kbar: torch.Tensor, N: int, topk: float, sc
     idx = torch.empty((B, H, n_qb, kk), dtype=torch.int32, device=dev)
     cnt = torch.empty((B, H, n_qb), dtype=torch.int32, device=dev)
     _check("sparge_predict_mask", load_library().sparge_predict_mask(
-        _ptr(qbar), _ptr(kbar), B, H, N, D, float(topk), _scale(scale, D), _ptr(mask), _ptr(idx),
-        _ptr(cnt), _stream(qbar)))
+        _ptr(qbar), _ptr(kbar), B, H, N, D, float(topk), _scale(scale, D), int(bool(is_causal)),
+        _ptr(mask), _ptr(idx), _ptr(cnt), _stream(qbar)))
     return mask, idx, cnt
 
 
@@ -229,7 +233,7 @@ def compact_mask(mask_id: torch.Tensor, N: int):
     return idx, cnt
 
 
-def attn_from_list(q, k, v, kv_idx=None, kv_cnt=None, scale=None, out=None):
+def attn_from_list(q, k, v, kv_idx=None, kv_cnt=None, scale=None, out=None, is_causal=False):
     """Attention over precomputed kept-block lists (kv_idx None: dense)."""
     q, k, v = _qkv(q, k, v)
     B, H, N, D = q.shape
@@ -244,12 +248,16 @@ def attn_from_list(q, k, v, kv_idx=None, kv_cnt=None, scale=None, out=None):
         ld = kv_idx.shape[3]
     _check("sparge_attn_from_list", load_library().sparge_attn_from_list(
         _ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt), ld, _ptr(out), B, H, N, D,
-        _strides(q), _strides(k), _strides(v), _strides(out), _scale(scale, D), _stream(q)))
+        _strides(q), _strides(k), _strides(v), _strides(out), _scale(scale, D), int(bool(is_causal)),
+        _stream(q)))
     return out
 
 
-def block_sparse_attn(q, k, v, mask_id=None, scale=None, out=None, workspace=None):
-    """Attention restricted to the 128x64 tiles a 0/1 mask_id selects (None: dense)."""
+def block_sparse_attn(q, k, v, mask_id=None, scale=None, out=None, workspace=None, is_causal=False):
+    """Attention restricted to the 128x64 tiles a 0/1 mask_id selects (None: dense).
+
+    With is_causal=True each query row also ignores the keys after it.
+    """
     q, k, v = _qkv(q, k, v)
     B, H, N, D = q.shape
     out = torch.empty_like(q) if out is None else out
@@ -261,18 +269,19 @@ def block_sparse_attn(q, k, v, mask_id=None, scale=None, out=None, workspace=Non
         nbytes = ws.numel() * ws.element_size()
     _check("block_sparse_attn", load_library().block_sparse_attn(
         _ptr(q), _ptr(k), _ptr(v), _ptr(mask_id), _ptr(out), B, H, N, D, _strides(q), _strides(k),
-        _strides(v), _strides(out), _scale(scale, D), _ptr(ws), nbytes, _stream(q)))
+        _strides(v), _strides(out), _scale(scale, D), int(bool(is_causal)), _ptr(ws), nbytes,
+        _stream(q)))
     return out
 
 
 def attn_topk(q, k, v, topk=0.5, is_causal=False, scale=None, return_mask=False, out=None,
               workspace=None):
-    """Top-k block-sparse attention; a drop-in for non-causal scaled dot-product attention.
+    """Top-k block-sparse attention; a drop-in for scaled dot-product attention.
 
-    Returns out, or (out, mask_id) with return_mask=True.
+    is_causal=True restricts each query block's candidates to the key blocks
+    its rows may see (keeping the top-k share of those) and masks later keys
+    per row. Returns out, or (out, mask_id) with return_mask=True.
     """
-    if is_causal:
-        raise NotImplementedError("causal attention is not supported (the method is non-causal)")
     q, k, v = _qkv(q, k, v)
     B, H, N, D = q.shape
     out = torch.empty_like(q) if out is None else out
@@ -280,6 +289,6 @@ def attn_topk(q, k, v, topk=0.5, is_causal=False, scale=None, return_mask=False,
     ws = _workspace(q, B, H, N, D, topk, workspace)
     _check("sparge_attn_topk", load_library().sparge_attn_topk(
         _ptr(q), _ptr(k), _ptr(v), float(topk), _ptr(out), B, H, N, D, _strides(q), _strides(k),
-        _strides(v), _strides(out), _scale(scale, D), _ptr(mask), _ptr(ws),
+        _strides(v), _strides(out), _scale(scale, D), int(bool(is_causal)), _ptr(mask), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(q)))
     return (out, mask) if return_mask else out

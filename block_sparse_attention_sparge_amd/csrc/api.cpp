@@ -146,6 +146,7 @@ sparge::AttnArgs attn_args(const uint16_t* q, const uint16_t* k, const uint16_t*
   a.vs = Strides{vs[0], vs[1], vs[2]};
   a.os = Strides{os[0], os[1], os[2]};
   a.scale = resolve_scale(scale, D);
+  a.causal = 0;
   return a;
 }
 
@@ -197,9 +198,10 @@ int sparge_pool_blocks(const uint16_t* x, int64_t B, int64_t H, int64_t N, int64
 }
 
 int sparge_predict_mask(const float* qbar, const float* kbar, int64_t B, int64_t H, int64_t N,
-                        int64_t D, double topk, float scale, uint8_t* mask_id, int32_t* kv_idx,
-                        int32_t* kv_cnt, void* stream) {
+                        int64_t D, double topk, float scale, int is_causal, uint8_t* mask_id,
+                        int32_t* kv_idx, int32_t* kv_cnt, void* stream) {
   if (!qbar || !kbar || !kv_idx || !kv_cnt) return SPARGE_ERR_NULL;
+  if (is_causal != 0 && is_causal != 1) return SPARGE_ERR_ARG;
   if (int rc = check_shape(B, H, N, D)) return rc;
   if (N > SPARGE_MAX_PREDICT_N) return SPARGE_ERR_SHAPE;
   int64_t k = 0;
@@ -216,9 +218,9 @@ int sparge_predict_mask(const float* qbar, const float* kbar, int64_t B, int64_t
     for (int j = i + 1; j < 3; ++j)
       if (overlap(outs[i], outs[j])) return SPARGE_ERR_ALIAS;
   }
-  return status_of(sparge::launch_predict(qbar, kbar, B * H, N, static_cast<int>(D), k,
-                                          resolve_scale(scale, D), mask_id, kv_idx, kv_cnt,
-                                          static_cast<hipStream_t>(stream)));
+  return status_of(sparge::launch_predict(qbar, kbar, B * H, N, static_cast<int>(D), k, topk,
+                                          is_causal, resolve_scale(scale, D), mask_id, kv_idx,
+                                          kv_cnt, static_cast<hipStream_t>(stream)));
 }
 
 int sparge_compact_mask(const uint8_t* mask_id, int64_t B, int64_t H, int64_t N, int32_t* kv_idx,
@@ -239,8 +241,9 @@ int sparge_attn_from_list(const uint16_t* q, const uint16_t* k, const uint16_t* 
                           uint16_t* out, int64_t B, int64_t H, int64_t N, int64_t D,
                           const int64_t q_strides[3], const int64_t k_strides[3],
                           const int64_t v_strides[3], const int64_t o_strides[3], float scale,
-                          void* stream) {
+                          int is_causal, void* stream) {
   if (int rc = check_attn(q, k, v, out, B, H, N, D, q_strides, k_strides, v_strides, o_strides)) return rc;
+  if (is_causal != 0 && is_causal != 1) return SPARGE_ERR_ARG;
   if (kv_idx) {
     if (!kv_cnt) return SPARGE_ERR_NULL;
     if (ld_idx < 1) return SPARGE_ERR_ARG;
@@ -254,6 +257,7 @@ int sparge_attn_from_list(const uint16_t* q, const uint16_t* k, const uint16_t* 
   a.kv_idx = kv_idx;
   a.kv_cnt = kv_idx ? kv_cnt : nullptr;
   a.ld_idx = kv_idx ? ld_idx : 0;
+  a.causal = is_causal;
   return status_of(sparge::launch_attention(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -261,9 +265,11 @@ int block_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       const uint8_t* mask_id, uint16_t* out, int64_t B, int64_t H, int64_t N,
                       int64_t D, const int64_t q_strides[3], const int64_t k_strides[3],
                       const int64_t v_strides[3], const int64_t o_strides[3], float scale,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+                      int is_causal, void* workspace, size_t workspace_bytes, void* stream) {
   if (int rc = check_attn(q, k, v, out, B, H, N, D, q_strides, k_strides, v_strides, o_strides)) return rc;
+  if (is_causal != 0 && is_causal != 1) return SPARGE_ERR_ARG;
   sparge::AttnArgs a = attn_args(q, k, v, out, B, H, N, D, q_strides, k_strides, v_strides, o_strides, scale);
+  a.causal = is_causal;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (!mask_id) return status_of(sparge::launch_attention(a, st));   // dense: no list needed
 
@@ -295,8 +301,10 @@ int sparge_attn_topk(const uint16_t* q, const uint16_t* k, const uint16_t* v, do
                      uint16_t* out, int64_t B, int64_t H, int64_t N, int64_t D,
                      const int64_t q_strides[3], const int64_t k_strides[3],
                      const int64_t v_strides[3], const int64_t o_strides[3], float scale,
-                     uint8_t* mask_out, void* workspace, size_t workspace_bytes, void* stream) {
+                     int is_causal, uint8_t* mask_out, void* workspace, size_t workspace_bytes,
+                     void* stream) {
   if (int rc = check_attn(q, k, v, out, B, H, N, D, q_strides, k_strides, v_strides, o_strides)) return rc;
+  if (is_causal != 0 && is_causal != 1) return SPARGE_ERR_ARG;
   if (N > SPARGE_MAX_PREDICT_N) return SPARGE_ERR_SHAPE;
   int64_t kk = 0;
   if (int rc = topk_count(n_kblocks(N), topk, &kk)) return rc;
@@ -326,13 +334,14 @@ int sparge_attn_topk(const uint16_t* q, const uint16_t* k, const uint16_t* v, do
   const Strides ks{k_strides[0], k_strides[1], k_strides[2]};
   if (int rc = status_of(sparge::launch_pool(q, B, H, N, static_cast<int>(D), qs, SPARGE_Q_BLOCK, qbar, st))) return rc;
   if (int rc = status_of(sparge::launch_pool(k, B, H, N, static_cast<int>(D), ks, SPARGE_K_BLOCK, kbar, st))) return rc;
-  if (int rc = status_of(sparge::launch_predict(qbar, kbar, B * H, N, static_cast<int>(D), kk, sc,
-                                                mask_out, idx, cnt, st)))
+  if (int rc = status_of(sparge::launch_predict(qbar, kbar, B * H, N, static_cast<int>(D), kk, topk,
+                                                is_causal, sc, mask_out, idx, cnt, st)))
     return rc;
   sparge::AttnArgs a = attn_args(q, k, v, out, B, H, N, D, q_strides, k_strides, v_strides, o_strides, sc);
   a.kv_idx = idx;
   a.kv_cnt = cnt;
   a.ld_idx = kk;
+  a.causal = is_causal;
   return status_of(sparge::launch_attention(a, st));
 }
 

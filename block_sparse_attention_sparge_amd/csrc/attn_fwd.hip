@@ -1,10 +1,12 @@
 // Block-sparse flash attention forward for gfx950 (MI355X).
 //
-// Non-causal softmax attention in which query block i (128 rows) visits only
+// Softmax attention in which query block i (128 rows) visits only
 // the 64-key blocks of its list (SpargeAttention Documentation,
 // block_sparse_sage2_attn_cuda and "Mask Requirements": fixed 128x64 tiles).
-// Skipped tiles are never loaded. Online softmax keeps a running max m and
-// sum l per query row and rescales the output accumulator in registers.
+// Skipped tiles are never loaded. With causal masking (the top-k API's
+// is_causal flag) a row also ignores the keys after it. Online softmax keeps a
+// running max m and sum l per query row and rescales the output accumulator in
+// registers.
 //
 // Work decomposition
 //   One workgroup = one query block of one head: 4 wavefronts x 32 query rows.
@@ -98,6 +100,7 @@ struct Params {
   int64_t per_xcd;     // query blocks per XCD slice of a head
   Strides qs, ks, vs, os;
   float c;             // scale * log2(e)
+  int causal;          // 1: row r sees keys c <= r only
 };
 
 // Row of the K tile that feeds A-operand row m, chosen so that accumulator
@@ -143,13 +146,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) char lds_v1[C::kTile];
 
   // Workgroup -> (head, query block). Consecutive workgroup ids go to
-  // consecutive XCDs; XCD x owns query blocks [x*per, (x+1)*per) of every head.
+  // consecutive XCDs. Non-causal lists are about equally long: XCD x owns query
+  // blocks [x*per, (x+1)*per) of every head, so neighbouring blocks, whose
+  // lists overlap, share its L2. Causal lists grow with the block index: each
+  // head's blocks are dispatched longest first and dealt round the XCDs, so
+  // short lists fill in at the end instead of one XCD carrying the long ones.
   const int64_t wid = blockIdx.x;
-  const int64_t xcd = wid % kNumXcd;
-  const int64_t it = wid / kNumXcd;
-  const int64_t bh = it / p.per_xcd;
-  const int64_t qb = xcd * p.per_xcd + (it - bh * p.per_xcd);
-  if (qb >= p.n_qb) return;
+  int64_t bh, qb;
+  if (!p.causal) {
+    const int64_t xcd = wid % kNumXcd;
+    const int64_t it = wid / kNumXcd;
+    bh = it / p.per_xcd;
+    qb = xcd * p.per_xcd + (it - bh * p.per_xcd);
+  } else {
+    const int64_t per_head = kNumXcd * p.per_xcd;
+    bh = wid / per_head;
+    qb = p.n_qb - 1 - (wid - bh * per_head);
+  }
+  if (qb < 0 || qb >= p.n_qb) return;
   const int64_t b = bh / p.H, h = bh - (bh / p.H) * p.H;
 
   const int t = threadIdx.x;
@@ -265,13 +279,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
     }
   };
 
-  // Keys past N in a ragged (or invalid) block take no weight.
-  auto mask_tail = [&](int64_t j, f32x16& s0, f32x16& s1) {
-    if (j * kKBlock + kKBlock > p.N) {
-      // register i of this lane holds key 8g + i (i < 8) or 8g + 16 + (i - 8);
-      // keys from lim on are masked
-      const int64_t lim64 = p.N - j * kKBlock;
-      const int lim = static_cast<int>(lim64 < 0 ? 0 : lim64) - 8 * g;
+  // Keys past N in a ragged (or invalid) block take no weight, and with causal
+  // masking neither do keys after this lane's query row. Only tiles at the
+  // sequence end or across the block's diagonal need the per-key test.
+  auto mask_keys = [&](int64_t j, f32x16& s0, f32x16& s1) {
+    const int64_t k0 = j * kKBlock;
+    if (k0 + kKBlock > p.N || (p.causal && k0 + kKBlock - 1 > qb * kQBlock)) {
+      // keys k0 + lim and later are masked; register i of this lane holds key
+      // 8g + i (i < 8) or 8g + 16 + (i - 8)
+      int64_t lim64 = p.N - k0;
+      if (p.causal && qrow - k0 + 1 < lim64) lim64 = qrow - k0 + 1;
+      const int lim = static_cast<int>(lim64 < 0 ? 0 : (lim64 > kKBlock ? kKBlock : lim64)) - 8 * g;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int kl = (i < 8) ? i : 16 + (i - 8);
@@ -392,7 +410,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
           }
         }
       });
-      mask_tail(j0, sa, sb);
+      mask_keys(j0, sa, sb);
       bf16x8 pb[4];
       weights(sa, sb, pb);
       pv(v_cur, pb);
@@ -441,6 +459,7 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   p.per_xcd = (p.n_qb + kNumXcd - 1) / kNumXcd;
   p.qs = a.qs; p.ks = a.ks; p.vs = a.vs; p.os = a.os;
   p.c = a.scale * kLog2e;
+  p.causal = a.causal;
   const int64_t grid = a.B * a.H * kNumXcd * p.per_xcd;
   void* args[] = {(void*)&p};
   return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<D>),

@@ -20,9 +20,12 @@ struct Strides {
 hipError_t launch_pool(const uint16_t* x, int64_t B, int64_t H, int64_t N, int D, Strides s,
                        int block_rows, float* out, hipStream_t stream);
 
+// k: the count of a row with all N_KB candidates (also the row stride of kv_idx).
+// causal: row i ranks key blocks 0 .. (last row of block i) / 64 only and keeps
+// the topk count of those (same rounding rule as the host's).
 hipError_t launch_predict(const float* qbar, const float* kbar, int64_t BH, int64_t N, int D,
-                          int64_t k, float scale, uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt,
-                          hipStream_t stream);
+                          int64_t k, double topk, int causal, float scale, uint8_t* mask,
+                          int32_t* kv_idx, int32_t* kv_cnt, hipStream_t stream);
 
 hipError_t launch_compact(const uint8_t* mask, int64_t rows, int64_t n_kb, int32_t* kv_idx,
                           int32_t* kv_cnt, hipStream_t stream);
@@ -39,6 +42,7 @@ struct AttnArgs {
   int D;
   Strides qs, ks, vs, os;
   float scale;
+  int causal;              // 1: row r sees keys c <= r only
 };
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);

@@ -7,6 +7,11 @@
 // mask row (mask_id of SpargeAttention Documentation, "Mask Requirements") and
 // the ascending list of kept key blocks that the attention kernel walks.
 //
+// Causal variant (the top-k API's is_causal flag): query block i ranks only the
+// key blocks 0 .. J(i) = (last row of the block) / 64, whose keys some of its
+// rows may see, and keeps ceil(topk * (J(i) + 1)) of them (the host's rounding
+// rule, evaluated here in double precision).
+//
 // One workgroup (4 wavefronts) takes R query blocks of one head. Scores for
 // all R rows live in LDS. Selection is an exact radix select on order-preserving
 // 32-bit keys (4 passes of 8 bits, LDS histograms, wavefront prefix sums), one
@@ -26,6 +31,15 @@ __device__ __forceinline__ uint32_t order_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// ceil(topk * n) in double, a product within 1e-9 of an integer counting as
+// that integer, clamped to [1, n]: the host's k for a row of n candidates.
+__device__ __forceinline__ int64_t topk_count_dev(int64_t n, double topk) {
+  const double x = topk * static_cast<double>(n);
+  const double r = __builtin_rint(x);
+  int64_t k = (__builtin_fabs(x - r) <= 1e-9) ? static_cast<int64_t>(r) : static_cast<int64_t>(__builtin_ceil(x));
+  return k < 1 ? 1 : (k > n ? n : k);
+}
+
 // Number of set bits of `m` in lanes below this lane.
 __device__ __forceinline__ uint32_t count_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
@@ -34,9 +48,9 @@ __device__ __forceinline__ uint32_t count_below(uint64_t m) {
 
 template <int D, int R>
 __global__ __launch_bounds__(kThreads) void predict_kernel(
-    const float* __restrict__ qbar, const float* __restrict__ kbar, int64_t n_qb, int64_t n_kb,
-    int64_t n_groups, int64_t k, float scale, uint8_t* __restrict__ mask,
-    int32_t* __restrict__ kv_idx, int32_t* __restrict__ kv_cnt) {
+    const float* __restrict__ qbar, const float* __restrict__ kbar, int64_t N, int64_t n_qb,
+    int64_t n_kb, int64_t n_groups, int64_t k, double topk, int causal, float scale,
+    uint8_t* __restrict__ mask, int32_t* __restrict__ kv_idx, int32_t* __restrict__ kv_cnt) {
   extern __shared__ float4 smem4[];
   float* q_lds = reinterpret_cast<float*>(smem4);          // [R][D]
   float* sc = q_lds + R * D;                               // [R][n_kb]
@@ -89,16 +103,23 @@ __global__ __launch_bounds__(kThreads) void predict_kernel(
     const int64_t qi = row0 + r;
     const bool active = (r < R) && (qi < n_qb);
     const float* srow = sc + (r < R ? r : 0) * n_kb;
+    // candidates [0, n_cand) and the number kept, k_row
+    int64_t n_cand = n_kb, k_row = k;
+    if (causal && active) {
+      const int64_t last_row = (qi + 1) * kQBlock < N ? (qi + 1) * kQBlock - 1 : N - 1;
+      n_cand = last_row / kKBlock + 1;
+      k_row = topk_count_dev(n_cand, topk);
+    }
 
     uint32_t prefix = 0, prefix_mask = 0;
-    int64_t kk = k;   // how many still to take among keys matching the prefix
+    int64_t kk = k_row;   // how many still to take among keys matching the prefix
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
 #pragma unroll
       for (int q = 0; q < 4; ++q) h[lane * 4 + q] = 0u;
       __syncthreads();
       if (active) {
-        for (int64_t j = lane; j < n_kb; j += 64) {
+        for (int64_t j = lane; j < n_cand; j += 64) {
           const uint32_t u = order_key(srow[j]);
           if ((u & prefix_mask) == prefix) atomicAdd(&h[(u >> shift) & 255u], 1u);
         }
@@ -141,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void predict_kernel(
       int64_t base = 0, eq_seen = 0;
       for (int64_t j0 = 0; j0 < n_kb; j0 += 64) {
         const int64_t j = j0 + lane;
-        const bool valid = j < n_kb;
+        const bool valid = j < n_cand;
         const uint32_t u = valid ? order_key(srow[j]) : 0u;
         const bool is_eq = valid && u == thr;
         const uint64_t eq_b = __ballot(is_eq);
@@ -149,52 +170,53 @@ __global__ __launch_bounds__(kThreads) void predict_kernel(
         const bool sel = valid && (u > thr || (is_eq && eq_rank < kk));
         const uint64_t sel_b = __ballot(sel);
         const int64_t pos = base + count_below(sel_b);
-        if (sel && pos < k) out_idx[pos] = static_cast<int32_t>(j);
-        if (out_mask && valid) out_mask[j] = sel ? 1 : 0;
+        if (sel && pos < k_row) out_idx[pos] = static_cast<int32_t>(j);
+        if (out_mask && j < n_kb) out_mask[j] = sel ? 1 : 0;
         base += __popcll(sel_b);
         eq_seen += __popcll(eq_b);
       }
-      if (lane == 0) kv_cnt[row] = static_cast<int32_t>(k);
+      if (lane == 0) kv_cnt[row] = static_cast<int32_t>(k_row);
     }
   }
 }
 
 template <int D, int R>
-hipError_t launch_predict_t(const float* qbar, const float* kbar, int64_t BH, int64_t n_qb,
-                            int64_t n_kb, int64_t k, float scale, uint8_t* mask, int32_t* kv_idx,
-                            int32_t* kv_cnt, hipStream_t stream) {
+hipError_t launch_predict_t(const float* qbar, const float* kbar, int64_t BH, int64_t N, int64_t n_qb,
+                            int64_t n_kb, int64_t k, double topk, int causal, float scale,
+                            uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt, hipStream_t stream) {
   const int64_t n_groups = (n_qb + R - 1) / R;
   const size_t lds = sizeof(float) * (R * D + R * n_kb) + sizeof(uint32_t) * kWaves * 256;
-  void* args[] = {(void*)&qbar, (void*)&kbar, (void*)&n_qb, (void*)&n_kb, (void*)&n_groups,
-                  (void*)&k, (void*)&scale, (void*)&mask, (void*)&kv_idx, (void*)&kv_cnt};
+  void* args[] = {(void*)&qbar, (void*)&kbar, (void*)&N, (void*)&n_qb, (void*)&n_kb,
+                  (void*)&n_groups, (void*)&k, (void*)&topk, (void*)&causal, (void*)&scale,
+                  (void*)&mask, (void*)&kv_idx, (void*)&kv_cnt};
   return hipLaunchKernel(reinterpret_cast<const void*>(&predict_kernel<D, R>),
                          dim3(static_cast<uint32_t>(BH * n_groups)), dim3(kThreads), args, lds,
                          stream);
 }
 
 template <int D>
-hipError_t launch_predict_d(const float* qbar, const float* kbar, int64_t BH, int64_t n_qb,
-                            int64_t n_kb, int64_t k, float scale, uint8_t* mask, int32_t* kv_idx,
-                            int32_t* kv_cnt, hipStream_t stream) {
+hipError_t launch_predict_d(const float* qbar, const float* kbar, int64_t BH, int64_t N, int64_t n_qb,
+                            int64_t n_kb, int64_t k, double topk, int causal, float scale,
+                            uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt, hipStream_t stream) {
   if (n_kb <= 1536)
-    return launch_predict_t<D, 8>(qbar, kbar, BH, n_qb, n_kb, k, scale, mask, kv_idx, kv_cnt, stream);
+    return launch_predict_t<D, 8>(qbar, kbar, BH, N, n_qb, n_kb, k, topk, causal, scale, mask, kv_idx, kv_cnt, stream);
   if (n_kb <= 3072)
-    return launch_predict_t<D, 4>(qbar, kbar, BH, n_qb, n_kb, k, scale, mask, kv_idx, kv_cnt, stream);
+    return launch_predict_t<D, 4>(qbar, kbar, BH, N, n_qb, n_kb, k, topk, causal, scale, mask, kv_idx, kv_cnt, stream);
   if (n_kb <= 6144)
-    return launch_predict_t<D, 2>(qbar, kbar, BH, n_qb, n_kb, k, scale, mask, kv_idx, kv_cnt, stream);
-  return launch_predict_t<D, 1>(qbar, kbar, BH, n_qb, n_kb, k, scale, mask, kv_idx, kv_cnt, stream);
+    return launch_predict_t<D, 2>(qbar, kbar, BH, N, n_qb, n_kb, k, topk, causal, scale, mask, kv_idx, kv_cnt, stream);
+  return launch_predict_t<D, 1>(qbar, kbar, BH, N, n_qb, n_kb, k, topk, causal, scale, mask, kv_idx, kv_cnt, stream);
 }
 
 }  // namespace
 
 hipError_t launch_predict(const float* qbar, const float* kbar, int64_t BH, int64_t N, int D,
-                          int64_t k, float scale, uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt,
-                          hipStream_t stream) {
+                          int64_t k, double topk, int causal, float scale, uint8_t* mask,
+                          int32_t* kv_idx, int32_t* kv_cnt, hipStream_t stream) {
   const int64_t n_qb = (N + kQBlock - 1) / kQBlock;
   const int64_t n_kb = (N + kKBlock - 1) / kKBlock;
   if (D == 128)
-    return launch_predict_d<128>(qbar, kbar, BH, n_qb, n_kb, k, scale, mask, kv_idx, kv_cnt, stream);
-  return launch_predict_d<64>(qbar, kbar, BH, n_qb, n_kb, k, scale, mask, kv_idx, kv_cnt, stream);
+    return launch_predict_d<128>(qbar, kbar, BH, N, n_qb, n_kb, k, topk, causal, scale, mask, kv_idx, kv_cnt, stream);
+  return launch_predict_d<64>(qbar, kbar, BH, N, n_qb, n_kb, k, topk, causal, scale, mask, kv_idx, kv_cnt, stream);
 }
 
 }  // namespace sparge

@@ -10,9 +10,16 @@
  *      ceil(topk * n_kblocks) best key blocks, ties going to the lower key-block
  *      index. The result is mask_id of shape (B, H, ceil(N/128), ceil(N/64))
  *      with 0/1 entries.
- *   2. Attention. Non-causal softmax attention in which query block i only sees
- *      the keys of the key blocks its mask row selects. Skipped 128x64 tiles
- *      are never read.
+ *   2. Attention. Softmax attention in which query block i only sees the keys
+ *      of the key blocks its mask row selects. Skipped 128x64 tiles are never
+ *      read.
+ * Causal variant (the top-k API's is_causal flag, same page; its meaning
+ * beyond the flag is this library's reading): key c is visible to query row r
+ * when c <= r. Query block i ranks only the key blocks 0 .. J(i) =
+ * floor(last row of block i / 64), keeps ceil(topk * (J(i) + 1)) of them (the
+ * same rounding rule as sparge_topk_count), and within the kept blocks each
+ * row sees its visible keys only; a row left with no visible kept key is
+ * written as zeros.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -26,6 +33,8 @@
  *  - D (head dimension) must be 64 or 128. N >= 1, B >= 1, H >= 1.
  *  - N_QB = ceil(N/128) query blocks and N_KB = ceil(N/64) key blocks.
  *  - scale <= 0 means the default 1/sqrt(D).
+ *  - is_causal is 0 (non-causal) or 1 (causal, see above); other values are
+ *    rejected with SPARGE_ERR_ARG.
  *  - Pointers are device pointers unless a parameter says otherwise. The
  *    caller owns every buffer. The library allocates no memory and keeps no
  *    state between calls.
@@ -96,19 +105,22 @@ int sparge_pool_blocks(const uint16_t *x, int64_t B, int64_t H, int64_t N, int64
 /* Pooled-block scoring and per-row top-k selection.
  *   qbar     (B, H, N_QB, D) fp32 contiguous (sparge_pool_blocks with 128).
  *   kbar     (B, H, N_KB, D) fp32 contiguous (sparge_pool_blocks with 64).
- *   topk     in (0, 1]; each row keeps k = sparge_topk_count(N_KB, topk) blocks.
+ *   topk     in (0, 1]; each row keeps k = sparge_topk_count(N_KB, topk) blocks
+ *            (causal: sparge_topk_count(J(i) + 1, topk) of blocks 0 .. J(i)).
  *   scale    logit scale (<= 0: 1/sqrt(D)); s[i][j] = scale * qbar_i . kbar_j
  *            in fp32. Selection ranks s, which ranks the row softmax the same way.
+ *   is_causal  0 or 1.
  *   mask_id  optional (NULL allowed): (B, H, N_QB, N_KB) uint8 contiguous, 1 for
  *            a kept block, 0 otherwise.
- *   kv_idx   (B, H, N_QB, k) int32 contiguous: the kept key-block ids of each
- *            row in ascending order.
- *   kv_cnt   (B, H, N_QB) int32: k for every row.
+ *   kv_idx   (B, H, N_QB, k) int32 contiguous, k = sparge_topk_count(N_KB, topk):
+ *            the kept key-block ids of each row in ascending order.
+ *   kv_cnt   (B, H, N_QB) int32: the number kept in each row (k, or the
+ *            row's causal count).
  * Ties in s go to the lower key-block index, so the result is deterministic.
- * Errors: NULL, SHAPE (also N > SPARGE_MAX_PREDICT_N), TOPK, ALIAS, LAUNCH. */
+ * Errors: NULL, SHAPE (also N > SPARGE_MAX_PREDICT_N), TOPK, ARG, ALIAS, LAUNCH. */
 int sparge_predict_mask(const float *qbar, const float *kbar, int64_t B, int64_t H, int64_t N,
-                        int64_t D, double topk, float scale, uint8_t *mask_id, int32_t *kv_idx,
-                        int32_t *kv_cnt, void *stream);
+                        int64_t D, double topk, float scale, int is_causal, uint8_t *mask_id,
+                        int32_t *kv_idx, int32_t *kv_cnt, void *stream);
 
 /* Mask compaction: each mask_id row becomes the ascending list of the key
  * blocks it selects (any nonzero byte counts as selected).
@@ -128,44 +140,47 @@ int sparge_compact_mask(const uint8_t *mask_id, int64_t B, int64_t H, int64_t N,
  *   out      (B, H, N, D) bf16 with strides o_strides; rows with an empty list
  *            are written as zeros.
  * O[r] = sum_c softmax_c(scale * Q[r] . K[c]) V[c] over the keys c of the listed
- * blocks (fp32 accumulation, probabilities rounded to bf16 before the PV
- * product, output rounded to nearest-even bf16).
+ * blocks (with is_causal = 1: the listed keys c <= r), with fp32 accumulation,
+ * probabilities rounded to bf16 before the PV product and the output rounded
+ * to nearest-even bf16.
  * Errors: NULL, SHAPE, STRIDE, ALIAS, ARG (ld_idx < 1), LAUNCH. */
 int sparge_attn_from_list(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                           const int32_t *kv_idx, const int32_t *kv_cnt, int64_t ld_idx,
                           uint16_t *out, int64_t B, int64_t H, int64_t N, int64_t D,
                           const int64_t q_strides[3], const int64_t k_strides[3],
                           const int64_t v_strides[3], const int64_t o_strides[3], float scale,
-                          void *stream);
+                          int is_causal, void *stream);
 
 /* Block-sparse attention with a given block mask
  * (SpargeAttention Documentation, block_sparse_sage2_attn_cuda and "Mask
  * Requirements"). mask_id is (B, H, N_QB, N_KB) uint8 contiguous with 0/1
  * entries (nonzero counts as 1), or NULL for dense attention. The mask is
- * compacted into the workspace, then attention runs over the listed tiles.
+ * compacted into the workspace, then attention runs over the listed tiles
+ * (with is_causal = 1 each row also ignores the keys after it).
  *   workspace   device buffer of at least sparge_workspace_bytes(B,H,N,D,-1).
- * Errors: NULL, SHAPE, STRIDE, ALIAS, WORKSPACE, LAUNCH. */
+ * Errors: NULL, SHAPE, STRIDE, ALIAS, ARG, WORKSPACE, LAUNCH. */
 int block_sparse_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                       const uint8_t *mask_id, uint16_t *out, int64_t B, int64_t H, int64_t N,
                       int64_t D, const int64_t q_strides[3], const int64_t k_strides[3],
                       const int64_t v_strides[3], const int64_t o_strides[3], float scale,
-                      void *workspace, size_t workspace_bytes, void *stream);
+                      int is_causal, void *workspace, size_t workspace_bytes, void *stream);
 
-/* Top-k block-sparse attention, a drop-in for non-causal scaled dot-product
- * attention (SpargeAttention Documentation, spas_sage2_attn_meansim_topk_cuda:
- * higher topk favours accuracy, lower topk sparsity). Runs pooling,
- * prediction and attention back to back on `stream`.
+/* Top-k block-sparse attention, a drop-in for scaled dot-product attention
+ * (SpargeAttention Documentation, spas_sage2_attn_meansim_topk_cuda: higher
+ * topk favours accuracy, lower topk sparsity; is_causal as described above).
+ * Runs pooling, prediction and attention back to back on `stream`.
  *   topk        in (0, 1].
  *   scale       used both for the pooled scores and for attention (<= 0: 1/sqrt(D)).
  *   mask_out    optional (NULL allowed): receives the predicted mask_id,
  *               (B, H, N_QB, N_KB) uint8 contiguous.
  *   workspace   device buffer of at least sparge_workspace_bytes(B,H,N,D,topk).
- * Errors: NULL, SHAPE, TOPK, STRIDE, ALIAS, WORKSPACE, LAUNCH. */
+ * Errors: NULL, SHAPE, TOPK, STRIDE, ALIAS, ARG, WORKSPACE, LAUNCH. */
 int sparge_attn_topk(const uint16_t *q, const uint16_t *k, const uint16_t *v, double topk,
                      uint16_t *out, int64_t B, int64_t H, int64_t N, int64_t D,
                      const int64_t q_strides[3], const int64_t k_strides[3],
                      const int64_t v_strides[3], const int64_t o_strides[3], float scale,
-                     uint8_t *mask_out, void *workspace, size_t workspace_bytes, void *stream);
+                     int is_causal, uint8_t *mask_out, void *workspace, size_t workspace_bytes,
+                     void *stream);
 
 #ifdef __cplusplus
 }

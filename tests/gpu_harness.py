@@ -42,7 +42,7 @@ def assert_close(got, ref, what=""):
     return r
 
 
-def oracle_mask_parity(q64_heads, k64_heads, topk, mask_dev, scale=None):
+def oracle_mask_parity(q64_heads, k64_heads, topk, mask_dev, scale=None, causal=False):
     """Run the oracle prediction per head and compare with a device mask.
 
     q64_heads / k64_heads: callables (b, h) -> (N, D) float64. mask_dev: (B, H, Qb, Kb) numpy.
@@ -53,9 +53,9 @@ def oracle_mask_parity(q64_heads, k64_heads, topk, mask_dev, scale=None):
     for b in range(B):
         for h in range(H):
             qh, kh = q64_heads(b, h), k64_heads(b, h)
-            pr = oracle.predict_mask(qh[None, None], kh[None, None], topk, scale)
+            pr = oracle.predict_mask(qh[None, None], kh[None, None], topk, scale, causal=causal)
             rep = oracle.mask_parity(pr["logits"], pr["mask"], mask_dev[b, h][None, None], pr["k"],
-                                     band=MASK_BAND, probs=pr["probs"])
+                                     band=MASK_BAND, probs=pr["probs"], cand=pr["cand"])
             for key in tot:
                 tot[key] += rep.get(key, 0)
     return tot

@@ -82,13 +82,13 @@ def contiguous(H, N, D):
 
 
 def attn_call(lib, fn, q=A, k=Bp, v=C, out=O, B=1, H=2, N=256, D=64, qs=None, ks=None, vs=None,
-              os_=None, mask=None, ws=0, wsb=0, topk=0.5):
+              os_=None, mask=None, ws=0, wsb=0, topk=0.5, causal=0):
     st = contiguous(H, N, D)
     qs, ks, vs, os_ = (x or st for x in (qs, ks, vs, os_))
     if fn == "topk":
-        return lib.sparge_attn_topk(q, k, v, topk, out, B, H, N, D, qs, ks, vs, os_, 0.0, mask, ws,
-                                    wsb, None)
-    return lib.block_sparse_attn(q, k, v, mask, out, B, H, N, D, qs, ks, vs, os_, 0.0, ws, wsb,
+        return lib.sparge_attn_topk(q, k, v, topk, out, B, H, N, D, qs, ks, vs, os_, 0.0, causal, mask,
+                                    ws, wsb, None)
+    return lib.block_sparse_attn(q, k, v, mask, out, B, H, N, D, qs, ks, vs, os_, 0.0, causal, ws, wsb,
                                  None)
 
 
@@ -106,6 +106,8 @@ def test_attention_argument_errors(lib, fn):
     assert attn_call(lib, fn, os_=S(2 * 256 * 64, 256 * 64, 32), mask=mask) == STRIDE  # rows overlap
     assert attn_call(lib, fn, out=A + 1024, mask=mask) == ALIAS                      # out inside q
     assert attn_call(lib, fn, out=C - 1024, mask=mask) == ALIAS                      # out runs into v
+    for bad in (2, -1):
+        assert attn_call(lib, fn, mask=mask, causal=bad, ws=W, wsb=1 << 30) == ARG
     assert attn_call(lib, fn, mask=mask, ws=0, wsb=0) == WORKSPACE
     assert attn_call(lib, fn, mask=mask, ws=W, wsb=16) == WORKSPACE
     need = sp.workspace_bytes(1, 2, 256, 64, 0.5 if fn == "topk" else None)
@@ -116,7 +118,7 @@ def test_attention_argument_errors(lib, fn):
         assert attn_call(lib, fn, N=786433, ws=W, wsb=1 << 40) == SHAPE              # beyond the predict limit
         assert lib.sparge_attn_topk(A, Bp, C, 0.5, O, 1, 2, 256, 64, contiguous(2, 256, 64),
                                     contiguous(2, 256, 64), contiguous(2, 256, 64),
-                                    contiguous(2, 256, 64), 0.0, A + 64, W, need, None) == ALIAS
+                                    contiguous(2, 256, 64), 0.0, 0, A + 64, W, need, None) == ALIAS
     else:
         assert attn_call(lib, fn, mask=O + 64, ws=W, wsb=need) == ALIAS                 # mask inside out
         assert attn_call(lib, fn, mask=W + 64, ws=W, wsb=need) == ALIAS                 # mask inside workspace
@@ -129,28 +131,29 @@ def test_pool_predict_compact_errors(lib):
     assert lib.sparge_pool_blocks(A, 1, 2, 256, 80, st, 128, O, None) == SHAPE
     assert lib.sparge_pool_blocks(A, 1, 2, 256, 64, S(1, 2, 3), 128, O, None) == STRIDE
     assert lib.sparge_pool_blocks(A, 1, 2, 256, 64, st, 128, A + 512, None) == ALIAS
-    assert lib.sparge_predict_mask(None, Bp, 1, 2, 256, 64, 0.5, 0.0, None, C, O, None) == NULL
-    assert lib.sparge_predict_mask(A, Bp, 1, 2, 256, 64, 0.5, 0.0, None, None, O, None) == NULL
-    assert lib.sparge_predict_mask(A, Bp, 1, 2, 256, 64, 2.0, 0.0, None, C, O, None) == TOPK
-    assert lib.sparge_predict_mask(A, Bp, 1, 2, 786433, 64, 0.5, 0.0, None, C, O, None) == SHAPE
-    assert lib.sparge_predict_mask(A, Bp, 1, 2, 256, 64, 0.5, 0.0, None, A + 4, O, None) == ALIAS
-    assert lib.sparge_predict_mask(A, Bp, 1, 2, 256, 64, 0.5, 0.0, C, C + 4, O, None) == ALIAS
+    assert lib.sparge_predict_mask(None, Bp, 1, 2, 256, 64, 0.5, 0.0, 0, None, C, O, None) == NULL
+    assert lib.sparge_predict_mask(A, Bp, 1, 2, 256, 64, 0.5, 0.0, 0, None, None, O, None) == NULL
+    assert lib.sparge_predict_mask(A, Bp, 1, 2, 256, 64, 2.0, 0.0, 0, None, C, O, None) == TOPK
+    assert lib.sparge_predict_mask(A, Bp, 1, 2, 786433, 64, 0.5, 0.0, 0, None, C, O, None) == SHAPE
+    assert lib.sparge_predict_mask(A, Bp, 1, 2, 256, 64, 0.5, 0.0, 0, None, A + 4, O, None) == ALIAS
+    assert lib.sparge_predict_mask(A, Bp, 1, 2, 256, 64, 0.5, 0.0, 0, C, C + 4, O, None) == ALIAS
+    assert lib.sparge_predict_mask(A, Bp, 1, 2, 256, 64, 0.5, 0.0, 3, None, C, O, None) == ARG
     assert lib.sparge_compact_mask(None, 1, 2, 256, Bp, C, None) == NULL
     assert lib.sparge_compact_mask(A, 1, 2, 0, Bp, C, None) == SHAPE
     assert lib.sparge_compact_mask(A, 1, 2, 256, A + 1, C, None) == ALIAS
     assert lib.sparge_attn_from_list(A, Bp, C, W, None, 4, O, 1, 2, 256, 64, st, st, st, st, 0.0,
-                                     None) == NULL
+                                     0, None) == NULL
     assert lib.sparge_attn_from_list(A, Bp, C, W, M, 0, O, 1, 2, 256, 64, st, st, st, st, 0.0,
-                                     None) == ARG
+                                     0, None) == ARG
     assert lib.sparge_attn_from_list(A, Bp, C, O + 64, M, 4, O, 1, 2, 256, 64, st, st, st, st, 0.0,
-                                     None) == ALIAS
+                                     0, None) == ALIAS
+    assert lib.sparge_attn_from_list(A, Bp, C, W, M, 4, O, 1, 2, 256, 64, st, st, st, st, 0.0,
+                                     5, None) == ARG
 
 
 def test_python_wrapper_rejects_without_gpu():
     import torch
     x = torch.zeros(1, 1, 128, 64, dtype=torch.bfloat16)
-    with pytest.raises(NotImplementedError):
-        sp.attn_topk(x, x, x, is_causal=True)
     with pytest.raises(NotImplementedError):
         sp.attn_topk(x.float(), x, x)
     with pytest.raises(ValueError):

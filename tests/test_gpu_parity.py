@@ -276,3 +276,86 @@ def test_wan14b_topk_sweep(gpu_lib, topk):
         got = synth.bf16_bits_to_f64(out.view(torch.int16)[b, h, torch.from_numpy(rows).cuda()].cpu().numpy().view(np.uint16))
         ref = oracle.masked_attention_rows(F64(q[b, h]), F64(k[b, h]), F64(v[b, h]), m[b, h], rows)
         assert_close(got, ref, f"topk {topk} head {(b, h)}")
+
+# ------------------------------------------------------------------ causal
+
+
+@pytest.mark.parametrize("B,H,N,D", SMALL + [(1, 2, 2000, 128)])
+@pytest.mark.parametrize("topk", [0.2, 0.5, 1.0])
+def test_causal_predict(gpu_lib, B, H, N, D, topk):
+    q, k, v = rand_qkv(B, H, N, D, seed=7 * N + D, q_scale=1 / math.sqrt(D))
+    dq, dk = to_dev(q), to_dev(k)
+    mask, idx, cnt = sp.predict_mask(sp.pool_blocks(dq, 128), sp.pool_blocks(dk, 64), N, topk,
+                                     is_causal=True)
+    m, idx, cnt = mask.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy()
+    rep = oracle_mask_parity(lambda b, h: F64(q[b, h]), lambda b, h: F64(k[b, h]), topk, m, causal=True)
+    assert rep["failures"] == 0, rep
+    cand = np.array([oracle.causal_key_blocks(N, i) for i in range(m.shape[2])])
+    kk = np.array([oracle.topk_count(int(c), topk) for c in cand])
+    assert (cnt == kk[None, None]).all()
+    assert (m.sum(-1) == kk[None, None]).all()
+    for b in range(B):
+        for h in range(H):
+            for i in range(m.shape[2]):
+                assert idx[b, h, i, : kk[i]].tolist() == np.flatnonzero(m[b, h, i]).tolist()
+
+
+@pytest.mark.parametrize("B,H,N,D", SMALL)
+def test_causal_user_mask(gpu_lib, B, H, N, D):
+    q, k, v = rand_qkv(B, H, N, D, seed=11 * N + D)
+    m = _random_mask(B, H, N, 0.5, seed=N + 1)
+    out = sp.block_sparse_attn(*_dev(q, k, v), mask_id=torch.from_numpy(m).cuda(), is_causal=True)
+    ref = oracle.masked_attention(F64(q), F64(k), F64(v), m, causal=True)
+    print(assert_close(to_host_f64(out), ref, f"causal user mask {B, H, N, D}"))
+
+
+@pytest.mark.parametrize("B,H,N,D", SMALL)
+def test_causal_dense_and_topk_one(gpu_lib, B, H, N, D):
+    q, k, v = rand_qkv(B, H, N, D, seed=13 * N + D)
+    dq, dk, dv = _dev(q, k, v)
+    dense = sp.block_sparse_attn(dq, dk, dv, mask_id=None, is_causal=True)
+    top1, mask = sp.attn_topk(dq, dk, dv, topk=1.0, is_causal=True, return_mask=True)
+    torch.cuda.synchronize()
+    m = mask.cpu().numpy()
+    cand = np.array([oracle.causal_key_blocks(N, i) for i in range(m.shape[2])])
+    assert (m.sum(-1) == cand[None, None]).all()
+    t = lambda a: torch.from_numpy(F64(a))
+    ref = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), is_causal=True).numpy()
+    assert_close(to_host_f64(dense), ref, "dense causal vs SDPA")
+    assert_close(to_host_f64(top1), ref, "topk 1.0 causal vs SDPA")
+    # same kept tiles, but the dense walk also visits the future blocks (all masked): equal values
+    assert np.abs(to_host_f64(dense) - to_host_f64(top1)).max() == 0.0
+
+
+@pytest.mark.parametrize("N", EDGE_N + [255, 256, 257])
+@pytest.mark.parametrize("D", [64, 128])
+def test_causal_edge_lengths(gpu_lib, N, D):
+    q, k, v = rand_qkv(1, 2, N, D, seed=N * 5 + D)
+    dq, dk, dv = _dev(q, k, v)
+    out, mask = sp.attn_topk(dq, dk, dv, topk=0.5, is_causal=True, return_mask=True)
+    m = mask.cpu().numpy()
+    ref = oracle.masked_attention(F64(q), F64(k), F64(v), m, causal=True)
+    assert_close(to_host_f64(out), ref, f"causal edge N={N}")
+    rep = oracle_mask_parity(lambda b, h: F64(q[b, h]), lambda b, h: F64(k[b, h]), 0.5, m, causal=True)
+    assert rep["failures"] == 0
+
+
+@pytest.mark.parametrize("cfg,topk", [(1, 0.5), (2, 0.4)], ids=["cfg1-topk0.5", "cfg2-topk0.4"])
+def test_causal_workload_parity(gpu_lib, cfg, topk):
+    """Causal top-k at a workload's full size: every mask row, sampled output rows."""
+    wl = synth.WORKLOADS[cfg]
+    print(f"causal workload {wl.describe()} topk={topk}", flush=True)
+    q, k, v = synth.make_qkv(wl, seed=0)
+    out, mask = sp.attn_topk(*_dev(q, k, v), topk=topk, is_causal=True, return_mask=True)
+    torch.cuda.synchronize()
+    m = mask.cpu().numpy()
+    rep = oracle_mask_parity(lambda b, h: F64(q[b, h]), lambda b, h: F64(k[b, h]), topk, m, causal=True)
+    print("mask parity", rep, flush=True)
+    assert rep["failures"] == 0
+    rng = np.random.default_rng(100 + cfg)
+    outs = out.view(torch.int16)
+    for b, h in sorted({(0, 0), (wl.B - 1, wl.H - 1)}):
+        rows = _sample_rows(wl.N, rng)
+        got = synth.bf16_bits_to_f64(outs[b, h, torch.from_numpy(rows).cuda()].cpu().numpy().view(np.uint16))
+        ref = oracle.masked_attention_rows(F64(q[b, h]), F64(k[b, h]), F64(v[b, h]), m[b, h], rows, causal=True)
+        print(assert_close(got, ref, f"causal cfg{cfg} head {(b, h)}"), flush=True)
