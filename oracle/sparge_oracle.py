@@ -35,6 +35,16 @@ floor((last row of block i) / 64); it keeps ceil(topk * (J(i) + 1)) of them
 the kept blocks each row attends to its visible keys only. A row left with no
 visible kept key outputs zeros.
 
+Token layouts (optional, around the whole method; Official repository for
+AB-Attention, "Optional cube layout"; Attention Mechanisms (LightX2V), Sol-Attn
+on Wan2.1, "Tuning and implementation"): video tokens of a T x H x W grid,
+stored raster order (w fastest) after a prefix of text tokens, may be reordered
+before attention and restored after it, so that 128-query and 64-key blocks
+cover compact spatiotemporal regions. Two orders are defined here: 4 x 4 x 4
+cubes (cubes in raster order of the cube grid, tokens in raster order inside a
+cube, partial cubes at the grid edges) and a Morton (Z-order) curve over
+(t, h, w); text tokens keep their places.
+
 Steps 1-3 are this build's plain reading of the API name meansim_topk: block
 means, a similarity between them, top-k. The pages name the method but do not
 spell it out. Step 4 is an exact mathematical result; any correct
@@ -305,3 +315,53 @@ def mask_parity(logits: np.ndarray, oracle_mask: np.ndarray, device_mask: np.nda
         pgap = np.where(kr < cr, ps[rows, kr - 1] - ps[rows, np.minimum(kr, kb - 1)], np.inf)
         rep["prob_domain_candidates"] = int((pgap < band).sum())
     return rep
+
+
+def cube_permutation(n_text: int, T: int, H: int, W: int, cube=(4, 4, 4)) -> np.ndarray:
+    """New position p holds old token perm[p]: text tokens first, unchanged, then the
+    video tokens cube by cube (cubes of cube = (ct, ch, cw) in raster order of the
+    cube grid; a cube cut by the grid edge keeps the tokens it has), raster order
+    (t, h, w; w fastest) inside each cube."""
+    ct, ch, cw = (int(c) for c in cube)
+    perm = list(range(n_text))
+    for t0 in range(0, T, ct):
+        for h0 in range(0, H, ch):
+            for w0 in range(0, W, cw):
+                for t in range(t0, min(T, t0 + ct)):
+                    for h in range(h0, min(H, h0 + ch)):
+                        for w in range(w0, min(W, w0 + cw)):
+                            perm.append(n_text + (t * H + h) * W + w)
+    return np.asarray(perm, dtype=np.int64)
+
+
+def morton_code(t: int, h: int, w: int) -> int:
+    """Bit interleave of (t, h, w): bit b of w goes to bit 3b, of h to 3b+1, of t to 3b+2."""
+    code = 0
+    for b in range(21):
+        code |= ((w >> b) & 1) << (3 * b)
+        code |= ((h >> b) & 1) << (3 * b + 1)
+        code |= ((t >> b) & 1) << (3 * b + 2)
+    return code
+
+
+def morton_permutation(n_text: int, T: int, H: int, W: int) -> np.ndarray:
+    """Text tokens first, unchanged, then the video tokens in increasing Morton code."""
+    keyed = []
+    for t in range(T):
+        for h in range(H):
+            for w in range(W):
+                keyed.append((morton_code(t, h, w), n_text + (t * H + h) * W + w))
+    keyed.sort()
+    return np.asarray(list(range(n_text)) + [i for _, i in keyed], dtype=np.int64)
+
+
+def permute_tokens(x: np.ndarray, perm: np.ndarray, inverse: bool = False) -> np.ndarray:
+    """Reorder the token axis (-2): out[p] = x[perm[p]]; inverse: out[perm[p]] = x[p]."""
+    x = np.asarray(x)
+    perm = np.asarray(perm, dtype=np.int64)
+    if not inverse:
+        return x[..., perm, :]
+    out = np.empty_like(x)
+    out[..., perm, :] = x
+    return out
+

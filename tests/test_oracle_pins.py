@@ -24,7 +24,8 @@ def _ns(**over):
     names = ["Q_BLOCK", "K_BLOCK", "num_blocks", "default_scale", "topk_count", "pool_blocks",
              "block_logits", "row_softmax", "select_topk", "predict_mask", "selected_keys",
              "attend_rows", "masked_attention", "masked_attention_rows", "compact_mask", "mask_parity",
-             "causal_key_blocks"]
+             "causal_key_blocks", "cube_permutation", "morton_code", "morton_permutation",
+             "permute_tokens"]
     d = {n: getattr(real_oracle, n) for n in names}
     d.update(over)
     return types.SimpleNamespace(**d)
@@ -366,9 +367,58 @@ def pin_causal_predict(o):
     assert o.mask_parity(r["logits"], r["mask"], r["mask"], r["k"], cand=r["cand"])["failures"] == 0
 
 
+def pin_token_layouts(o):
+    for row in _golden("token_layouts.txt"):
+        colon = row.index(":")
+        head, want = row[:colon], [int(x) for x in row[colon + 1:]]
+        if head[0] == "cube":
+            n_text, T, H, W, ct, ch, cw = (int(x) for x in head[1:])
+            got = o.cube_permutation(n_text, T, H, W, (ct, ch, cw))
+        else:
+            n_text, T, H, W = (int(x) for x in head[1:])
+            got = o.morton_permutation(n_text, T, H, W)
+        assert got.tolist() == want, head
+    # bijections on ragged grids
+    for n_text, T, H, W in ((0, 5, 6, 7), (3, 4, 9, 13), (226, 3, 6, 9)):
+        n = n_text + T * H * W
+        for perm in (o.cube_permutation(n_text, T, H, W), o.morton_permutation(n_text, T, H, W)):
+            assert sorted(perm.tolist()) == list(range(n))
+            assert perm[:n_text].tolist() == list(range(n_text))
+    # full 4x4x4 cubes are 64 consecutive positions covering one box
+    T, H, W = 8, 8, 12
+    perm = o.cube_permutation(0, T, H, W)
+    for c in range(T * H * W // 64):
+        tok = perm[64 * c: 64 * c + 64]
+        t, h, w = tok // (H * W), (tok // W) % H, tok % W
+        assert np.ptp(t) == 3 and np.ptp(h) == 3 and np.ptp(w) == 3
+        assert t.min() % 4 == 0 and h.min() % 4 == 0 and w.min() % 4 == 0
+    # Morton on a 4x4x4 grid: every aligned group of 8 is a 2x2x2 box, the first one at the corner
+    perm = o.morton_permutation(0, 4, 4, 4)
+    for g in range(8):
+        tok = perm[8 * g: 8 * g + 8]
+        t, h, w = tok // 16, (tok // 4) % 4, tok % 4
+        assert np.ptp(t) == 1 and np.ptp(h) == 1 and np.ptp(w) == 1
+    assert sorted(perm[:8].tolist()) == [0, 1, 4, 5, 16, 17, 20, 21]
+    assert o.morton_code(1, 0, 0) == 4 and o.morton_code(0, 1, 0) == 2 and o.morton_code(0, 0, 2) == 8
+    # gather / scatter round trip, and scatter equals the gather by the inverse permutation
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((2, 3, 226 + 3 * 6 * 9, 4))
+    perm = o.cube_permutation(226, 3, 6, 9)
+    y = o.permute_tokens(x, perm)
+    assert np.array_equal(y[..., 5, :], x[..., perm[5], :])
+    assert np.array_equal(o.permute_tokens(y, perm, inverse=True), x)
+    assert np.array_equal(o.permute_tokens(y, perm, inverse=True), y[..., np.argsort(perm), :])
+    # dense non-causal attention commutes with a token permutation applied to q, k and v
+    q, k, v = (rng.standard_normal((1, 1, 300, 8)) for _ in range(3))
+    perm = o.morton_permutation(12, 2, 8, 18)
+    ones = np.ones((1, 1, 3, 5), dtype=np.uint8)
+    a = o.masked_attention(o.permute_tokens(q, perm), o.permute_tokens(k, perm), o.permute_tokens(v, perm), ones)
+    assert np.abs(o.permute_tokens(a, perm, inverse=True) - o.masked_attention(q, k, v, ones)).max() <= 1e-12
+
+
 PINS = [pin_block_counts, pin_topk_count, pin_pool, pin_scores, pin_select, pin_predict,
         pin_predict_ties, pin_attention, pin_attention_closed_forms, pin_attention_rows,
-        pin_compact, pin_mask_parity, pin_causal_attention, pin_causal_predict]
+        pin_compact, pin_mask_parity, pin_causal_attention, pin_causal_predict, pin_token_layouts]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -456,6 +506,36 @@ def _broken_variants():
                 out[r] = o.row_softmax(lg[r, c]) @ vs[c]
         return out
 
+    def cube_w_major(n_text, T, H, W, cube=(4, 4, 4)):
+        ct, ch, cw = cube
+        perm = list(range(n_text))
+        for t0 in range(0, T, ct):
+            for h0 in range(0, H, ch):
+                for w0 in range(0, W, cw):
+                    for w in range(w0, min(W, w0 + cw)):
+                        for h in range(h0, min(H, h0 + ch)):
+                            for t in range(t0, min(T, t0 + ct)):
+                                perm.append(n_text + (t * H + h) * W + w)
+        return np.asarray(perm)
+
+    def cube_drops_partial(n_text, T, H, W, cube=(4, 4, 4)):
+        ct, ch, cw = cube
+        perm = list(range(n_text))
+        for t0 in range(0, T - ct + 1, ct):
+            for h0 in range(0, H - ch + 1, ch):
+                for w0 in range(0, W - cw + 1, cw):
+                    for t in range(t0, t0 + ct):
+                        for h in range(h0, h0 + ch):
+                            for w in range(w0, w0 + cw):
+                                perm.append(n_text + (t * H + h) * W + w)
+        return np.asarray(perm)
+
+    def morton_t_lowest(t, h, w):
+        return o.morton_code(w, h, t)
+
+    def inverse_as_gather(x, perm, inverse=False):
+        return np.asarray(x)[..., np.asarray(perm), :]
+
     def causal_first_row(n, i):
         return (128 * i) // 64 + 1
 
@@ -480,6 +560,10 @@ def _broken_variants():
         "K used in place of V": dict(attend_rows=attend_transposed_v),
         "parity without the near-tie band": dict(mask_parity=parity_no_band),
         "causal row does not see its own key": dict(attend_rows=attend_causal_strict),
+        "cube order w-major inside a cube": dict(cube_permutation=cube_w_major),
+        "cube order drops the partial edge cubes": dict(cube_permutation=cube_drops_partial),
+        "Morton code with t as the lowest bit": dict(morton_code=morton_t_lowest),
+        "inverse permutation applied as a gather": dict(permute_tokens=inverse_as_gather),
         "causal candidates from the block's first row": dict(causal_key_blocks=causal_first_row),
         "causal candidates include future blocks": dict(causal_key_blocks=causal_all_blocks),
     }, src
