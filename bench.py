@@ -52,6 +52,11 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--causal", action="store_true", help="causal variant (is_causal=True)")
+    p.add_argument("--layout", choices=["raster", "cube", "morton"], default="raster",
+                   help="token order for the video grid: the step reorders Q, K, V, attends, restores O")
+    p.add_argument("--recall-rows", type=int, default=0,
+                   help="also report, for this many sampled rows of head 0, the share of the exact "
+                        "attention weight that falls in the kept blocks")
     p.add_argument("--kernels-only", action="store_true",
                    help="launch each kernel once plus a plain copy of known size, for counter runs")
     return p.parse_args()
@@ -87,6 +92,22 @@ def effective_flops(mask: np.ndarray, N: int, D: int, causal: bool = False) -> f
     qb, kb = mask.shape[-2:]
     pairs = tile_pairs(N, causal)
     return 4.0 * D * float((mask.reshape(-1, qb, kb).astype(np.float64) * pairs[None]).sum())
+
+
+def recall_share(qh, kh, mask_h, rows, scale, causal):
+    """Mean, over sampled query rows, of the exact softmax weight (over every visible key)
+    that falls on the keys of the kept blocks: how much of the attention the selection keeps."""
+    n = qh.shape[0]
+    shares = []
+    for r in rows:
+        lg = scale * (kh @ qh[r])
+        if causal:
+            lg[r + 1:] = -np.inf
+        w = np.exp(lg - lg.max())
+        w /= w.sum()
+        kept = np.repeat(mask_h[r // 128].astype(bool), 64)[:n]
+        shares.append(float(w[kept].sum()))
+    return {"rows": int(len(rows)), "mean": float(np.mean(shares)), "min": float(np.min(shares))}
 
 
 def kernel_durations_ms(fn, iters):
@@ -199,9 +220,25 @@ def main():
     kk = sp.topk_count(mask.shape[-1], topk)
 
     causal = bool(args.causal)
+    layout = args.layout
+    if layout != "raster":
+        if causal or wl.grid is None:
+            raise SystemExit("--layout needs a video workload and non-causal attention")
+        perm = sp.token_permutation(wl.n_text, wl.grid, layout)
+        dperm = perm.to(dev)
+        # the timed step starts from raster-order inputs and ends with a raster-order output
+        rq, rk, rv = dq, dk, dv
+        dq, dk, dv = (torch.empty_like(t) for t in (rq, rk, rv))
+        out_l = torch.empty_like(out)
 
     def step():
-        sp.attn_topk(dq, dk, dv, topk=topk, out=out, workspace=ws, is_causal=causal)
+        if layout == "raster":
+            sp.attn_topk(dq, dk, dv, topk=topk, out=out, workspace=ws, is_causal=causal)
+            return
+        for src, dst in ((rq, dq), (rk, dk), (rv, dv)):
+            sp.permute_tokens(src, dperm, out=dst)
+        sp.attn_topk(dq, dk, dv, topk=topk, out=out_l, workspace=ws)
+        sp.permute_tokens(out_l, dperm, inverse=True, out=out)
 
     # mask and lists once, for the per-kernel timings and the flop count
     step()
@@ -254,6 +291,19 @@ def main():
     pool_k = kernel_durations_ms(lambda: sp.pool_blocks(dk, 64), 10)
     pred = kernel_durations_ms(lambda: sp.predict_mask(qbar, kbar, N, topk, return_mask=True,
                                                        is_causal=causal), 10)
+    layout_info = {"name": layout}
+    if layout != "raster":
+        perm_ms = float(np.mean(kernel_durations_ms(lambda: sp.permute_tokens(rq, dperm, out=dq), 10)))
+        layout_info.update({"permute_ms": perm_ms,
+                            "permute_gbs": 2 * B * H * N * D * 2 / (perm_ms * 1e-3) / 1e9})
+    if args.recall_rows > 0:
+        qh = synth.bf16_bits_to_f64(q[0, 0])
+        kh = synth.bf16_bits_to_f64(k[0, 0])
+        if layout != "raster":
+            p_np = perm.numpy().astype(np.int64)
+            qh, kh = qh[p_np], kh[p_np]
+        rows = np.random.default_rng(7).choice(N, size=min(N, args.recall_rows), replace=False)
+        layout_info["recall"] = recall_share(qh, kh, m[0, 0], rows, 1.0 / np.sqrt(D), causal)
     bsa = kernel_durations_ms(lambda: sp.block_sparse_attn(dq, dk, dv, mask_id=mask_t, out=out,
                                                            is_causal=causal), 5)
 
@@ -277,7 +327,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "H": H, "N": N, "D": D, "topk": topk, "k": kk,
-                   "causal": causal,
+                   "causal": causal, "layout": layout,
                    "n_qblocks": int(qb_), "n_kblocks": int(kb_), "seed": args.seed,
                    "step": "sparge_attn_topk (pool Q, pool K, predict, attention)"},
         "dense_equiv_tflops": dense / (ms * 1e-3) / 1e12,
@@ -293,9 +343,10 @@ def main():
         "predict": {"ms": float(np.mean(pred)),
                     "gflops_fp32": pred_flops / (np.mean(pred) * 1e-3) / 1e9,
                     "gbs": pred_bytes / (np.mean(pred) * 1e-3) / 1e9},
+        "layout": layout_info,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": None if causal else load_traffic(f"{wl.name}_topk{topk}"),
+                     "traffic": None if (causal or layout != "raster") else load_traffic(f"{wl.name}_topk{topk}"),
                      "kernel": f"attn_fwd_kernel<{D}> (sparge_attn_from_list)"},
     }
     if not args.no_cpu_baseline:

@@ -82,6 +82,8 @@ def load_library() -> ctypes.CDLL:
                                    ci, vp, sz, vp]),
         "sparge_attn_topk": (ci, [vp, vp, vp, f64, vp, i64, i64, i64, i64, s3, s3, s3, s3, f32,
                                   ci, vp, vp, sz, vp]),
+        "sparge_token_permutation": (ci, [i64, i64, i64, i64, ci, s3, vp]),
+        "sparge_permute_tokens": (ci, [vp, vp, vp, i64, i64, i64, i64, s3, s3, ci, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -292,3 +294,36 @@ def attn_topk(q, k, v, topk=0.5, is_causal=False, scale=None, return_mask=False,
         _strides(v), _strides(out), _scale(scale, D), int(bool(is_causal)), _ptr(mask), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(q)))
     return (out, mask) if return_mask else out
+
+
+LAYOUTS = {"raster": 0, "cube": 1, "morton": 2}
+
+
+def token_permutation(n_text: int, grid, layout: str = "cube", cube=(4, 4, 4)) -> torch.Tensor:
+    """Host-computed token order for a text prefix plus a (T, H, W) video grid:
+    new position p holds old token perm[p]. Returns an int32 CPU tensor."""
+    T, Hh, Ww = (int(g) for g in grid)
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
+    n = int(n_text) + T * Hh * Ww
+    perm = torch.empty(n, dtype=torch.int32)
+    c3 = (ctypes.c_int64 * 3)(*[int(c) for c in cube])
+    _check("sparge_token_permutation", load_library().sparge_token_permutation(
+        int(n_text), T, Hh, Ww, LAYOUTS[layout], c3, perm.data_ptr()))
+    return perm
+
+
+def permute_tokens(x: torch.Tensor, perm: torch.Tensor, inverse: bool = False, out=None) -> torch.Tensor:
+    """Reorder the token axis of a (B, H, N, D) bf16 tensor: out[..., p, :] = x[..., perm[p], :]
+    (inverse=True: out[..., perm[p], :] = x[..., p, :]). perm: int32 on x's device."""
+    x = _operand(x, "x")
+    B, H, N, D = x.shape
+    if perm.dtype != torch.int32 or perm.device != x.device or perm.numel() != N:
+        raise ValueError("perm must be an int32 tensor of N entries on x's device")
+    perm = perm.contiguous()
+    out = torch.empty_like(x) if out is None else out
+    _check("sparge_permute_tokens", load_library().sparge_permute_tokens(
+        _ptr(x), _ptr(perm), _ptr(out), B, H, N, D, _strides(x), _strides(out), int(bool(inverse)),
+        _stream(x)))
+    return out
+

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsparge.so")
-SOURCES = ["pool.hip", "predict.hip", "compact.hip", "attn_fwd.hip", "api.cpp"]
+SOURCES = ["pool.hip", "predict.hip", "compact.hip", "attn_fwd.hip", "permute.hip", "api.cpp"]
 ARCH = "gfx950"
 
 

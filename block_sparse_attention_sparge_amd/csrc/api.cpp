@@ -8,6 +8,8 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <utility>
+#include <vector>
 
 #include "common.h"
 
@@ -343,6 +345,73 @@ int sparge_attn_topk(const uint16_t* q, const uint16_t* k, const uint16_t* v, do
   a.ld_idx = kk;
   a.causal = is_causal;
   return status_of(sparge::launch_attention(a, st));
+}
+
+int sparge_token_permutation(int64_t n_text, int64_t T, int64_t Hh, int64_t Ww, int layout,
+                             const int64_t cube[3], int32_t* perm) {
+  if (!perm) return SPARGE_ERR_NULL;
+  if (n_text < 0 || T < 1 || Hh < 1 || Ww < 1) return SPARGE_ERR_ARG;
+  if (T > kMaxDim || Hh > kMaxDim || Ww > kMaxDim || n_text > kMaxDim) return SPARGE_ERR_ARG;
+  const int64_t video = T * Hh * Ww;
+  if (video > (int64_t(1) << 31) - 1 - n_text || T * Hh > kMaxDim) return SPARGE_ERR_ARG;
+  if (layout != SPARGE_LAYOUT_RASTER && layout != SPARGE_LAYOUT_CUBE && layout != SPARGE_LAYOUT_MORTON)
+    return SPARGE_ERR_ARG;
+  if (layout == SPARGE_LAYOUT_CUBE && (!cube || cube[0] < 1 || cube[1] < 1 || cube[2] < 1))
+    return SPARGE_ERR_ARG;
+  if (layout == SPARGE_LAYOUT_MORTON && std::max({T, Hh, Ww}) > (int64_t(1) << 21)) return SPARGE_ERR_ARG;
+  int64_t pos = 0;
+  for (; pos < n_text; ++pos) perm[pos] = static_cast<int32_t>(pos);
+  auto token = [&](int64_t t, int64_t h, int64_t w) { return n_text + (t * Hh + h) * Ww + w; };
+  if (layout == SPARGE_LAYOUT_RASTER) {
+    for (int64_t i = 0; i < video; ++i) perm[pos++] = static_cast<int32_t>(n_text + i);
+  } else if (layout == SPARGE_LAYOUT_CUBE) {
+    const int64_t ct = cube[0], ch = cube[1], cw = cube[2];
+    for (int64_t t0 = 0; t0 < T; t0 += ct)
+      for (int64_t h0 = 0; h0 < Hh; h0 += ch)
+        for (int64_t w0 = 0; w0 < Ww; w0 += cw)
+          for (int64_t t = t0; t < std::min(T, t0 + ct); ++t)
+            for (int64_t h = h0; h < std::min(Hh, h0 + ch); ++h)
+              for (int64_t w = w0; w < std::min(Ww, w0 + cw); ++w)
+                perm[pos++] = static_cast<int32_t>(token(t, h, w));
+  } else {
+    // Z-order: bit b of w, h, t lands on bit 3b, 3b+1, 3b+2 of the key
+    auto spread = [](uint64_t v) {
+      uint64_t r = 0;
+      for (int b = 0; b < 21; ++b) r |= ((v >> b) & 1u) << (3 * b);
+      return r;
+    };
+    std::vector<std::pair<uint64_t, int32_t>> keyed;
+    keyed.reserve(static_cast<size_t>(video));
+    for (int64_t t = 0; t < T; ++t)
+      for (int64_t h = 0; h < Hh; ++h)
+        for (int64_t w = 0; w < Ww; ++w)
+          keyed.emplace_back(spread(w) | (spread(h) << 1) | (spread(t) << 2),
+                             static_cast<int32_t>(token(t, h, w)));
+    std::sort(keyed.begin(), keyed.end());
+    for (const auto& kv : keyed) perm[pos++] = kv.second;
+  }
+  return SPARGE_OK;
+}
+
+int sparge_permute_tokens(const uint16_t* x, const int32_t* perm, uint16_t* out, int64_t B, int64_t H,
+                          int64_t N, int64_t D, const int64_t x_strides[3],
+                          const int64_t out_strides[3], int inverse, void* stream) {
+  if (!x || !perm || !out) return SPARGE_ERR_NULL;
+  if (int rc = check_shape(B, H, N, D)) return rc;
+  if (int rc = check_strides(x_strides)) return rc;
+  if (int rc = check_strides(out_strides)) return rc;
+  if (inverse != 0 && inverse != 1) return SPARGE_ERR_ARG;
+  if (N > (int64_t(1) << 31) - 1) return SPARGE_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(out)) return SPARGE_ERR_STRIDE;
+  if (!non_overlapping(B, H, N, D, out_strides)) return SPARGE_ERR_STRIDE;
+  const Range ro = range_bf16(out, B, H, N, D, out_strides);
+  if (overlap(ro, range_bf16(x, B, H, N, D, x_strides)) ||
+      overlap(ro, range_bytes(perm, static_cast<size_t>(N) * sizeof(int32_t))))
+    return SPARGE_ERR_ALIAS;
+  const Strides xs{x_strides[0], x_strides[1], x_strides[2]};
+  const Strides os{out_strides[0], out_strides[1], out_strides[2]};
+  return status_of(sparge::launch_permute(x, xs, perm, out, os, B, H, N, static_cast<int>(D), inverse,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

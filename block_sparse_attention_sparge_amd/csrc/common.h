@@ -47,4 +47,10 @@ struct AttnArgs {
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
 
+// Gather (inverse = 0: out row p = x row perm[p]) or scatter (inverse = 1:
+// out row perm[p] = x row p) of whole token rows; entries outside [0, N) move nothing.
+hipError_t launch_permute(const uint16_t* x, Strides xs, const int32_t* perm, uint16_t* out,
+                          Strides os, int64_t B, int64_t H, int64_t N, int D, int inverse,
+                          hipStream_t stream);
+
 }  // namespace sparge

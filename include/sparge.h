@@ -182,6 +182,45 @@ int sparge_attn_topk(const uint16_t *q, const uint16_t *k, const uint16_t *v, do
                      int is_causal, uint8_t *mask_out, void *workspace, size_t workspace_bytes,
                      void *stream);
 
+/* Token layouts for sparge_token_permutation. */
+#define SPARGE_LAYOUT_RASTER 0   /* identity */
+#define SPARGE_LAYOUT_CUBE 1     /* video tokens cube by cube */
+#define SPARGE_LAYOUT_MORTON 2   /* video tokens along a Morton (Z-order) curve */
+
+/* Host-only helper: a token order that groups video tokens into compact
+ * spatiotemporal regions, so that 128-query and 64-key blocks cover nearby
+ * tokens (Official repository for AB-Attention, "Optional cube layout": 4x4x4
+ * spatiotemporal cubes; Attention Mechanisms (LightX2V), Sol-Attn on Wan2.1,
+ * "Tuning and implementation": Morton3D ordering). The sequence is n_text text
+ * tokens followed by a T x Hh x Ww video grid in raster order (w fastest).
+ *   layout  SPARGE_LAYOUT_RASTER: identity. SPARGE_LAYOUT_CUBE: the text tokens,
+ *           then the video tokens cube by cube, cubes of cube[0] x cube[1] x
+ *           cube[2] (t, h, w) in raster order of the cube grid (a cube cut by
+ *           the grid edge keeps the tokens it has), raster order inside a cube.
+ *           SPARGE_LAYOUT_MORTON: the text tokens, then the video tokens by
+ *           increasing Morton code (bit b of w, h, t at bits 3b, 3b+1, 3b+2).
+ *   cube    int64[3] host array, used by SPARGE_LAYOUT_CUBE only (NULL allowed otherwise).
+ *   perm    host array of n_text + T*Hh*Ww int32 the call fills: new position p
+ *           holds old token perm[p].
+ * Errors: NULL, ARG (negative n_text, empty grid, more than 2^31 - 1 tokens,
+ * unknown layout, cube sides < 1, a Morton side beyond 2^21). Makes no HIP call. */
+int sparge_token_permutation(int64_t n_text, int64_t T, int64_t Hh, int64_t Ww, int layout,
+                             const int64_t cube[3], int32_t *perm);
+
+/* Reorders the token axis of a (B, H, N, D) bf16 tensor by a permutation.
+ *   x, x_strides      input, strides as for the attention calls.
+ *   perm              device int32[N], a permutation of [0, N) (as from
+ *                     sparge_token_permutation); an entry outside [0, N) moves nothing.
+ *   out, out_strides  output, must not overlap x or perm.
+ *   inverse           0: out[:, :, p] = x[:, :, perm[p]] (into the new order);
+ *                     1: out[:, :, perm[p]] = x[:, :, p] (back to the old order).
+ * With a perm that is not a permutation, rows of out may be left unwritten or
+ * written twice (no out-of-bounds access either way).
+ * Errors: NULL, SHAPE, STRIDE, ALIAS, ARG (inverse not 0/1), LAUNCH. */
+int sparge_permute_tokens(const uint16_t *x, const int32_t *perm, uint16_t *out, int64_t B, int64_t H,
+                          int64_t N, int64_t D, const int64_t x_strides[3],
+                          const int64_t out_strides[3], int inverse, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

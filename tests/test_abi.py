@@ -151,6 +151,19 @@ def test_pool_predict_compact_errors(lib):
                                      5, None) == ARG
 
 
+def test_permute_tokens_errors(lib):
+    st = contiguous(2, 256, 64)
+    assert lib.sparge_permute_tokens(None, Bp, O, 1, 2, 256, 64, st, st, 0, None) == NULL
+    assert lib.sparge_permute_tokens(A, None, O, 1, 2, 256, 64, st, st, 0, None) == NULL
+    assert lib.sparge_permute_tokens(A, Bp, O, 1, 2, 256, 96, st, st, 0, None) == SHAPE
+    assert lib.sparge_permute_tokens(A, Bp, O, 1, 2, 256, 64, S(1, 2, 3), st, 0, None) == STRIDE
+    assert lib.sparge_permute_tokens(A + 8, Bp, O, 1, 2, 256, 64, st, st, 0, None) == STRIDE
+    assert lib.sparge_permute_tokens(A, Bp, O, 1, 2, 256, 64, st, S(256 * 64, 256 * 64, 32), 0, None) == STRIDE
+    assert lib.sparge_permute_tokens(A, Bp, O, 1, 2, 256, 64, st, st, 2, None) == ARG
+    assert lib.sparge_permute_tokens(A, Bp, A + 4096, 1, 2, 256, 64, st, st, 0, None) == ALIAS
+    assert lib.sparge_permute_tokens(A, O + 64, O, 1, 2, 256, 64, st, st, 0, None) == ALIAS
+
+
 def test_python_wrapper_rejects_without_gpu():
     import torch
     x = torch.zeros(1, 1, 128, 64, dtype=torch.bfloat16)

@@ -359,3 +359,63 @@ def test_causal_workload_parity(gpu_lib, cfg, topk):
         got = synth.bf16_bits_to_f64(outs[b, h, torch.from_numpy(rows).cuda()].cpu().numpy().view(np.uint16))
         ref = oracle.masked_attention_rows(F64(q[b, h]), F64(k[b, h]), F64(v[b, h]), m[b, h], rows, causal=True)
         print(assert_close(got, ref, f"causal cfg{cfg} head {(b, h)}"), flush=True)
+
+
+# ------------------------------------------------------------ token layouts
+
+
+@pytest.mark.parametrize("layout", ["cube", "morton"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_permute_tokens(gpu_lib, layout, D):
+    n_text, grid = 37, (5, 9, 14)
+    N = n_text + grid[0] * grid[1] * grid[2]
+    q, _, _ = rand_qkv(2, 3, N, D, seed=61 + D)
+    perm = sp.token_permutation(n_text, grid, layout)
+    dperm = perm.cuda()
+    x = to_dev(q)
+    y = sp.permute_tokens(x, dperm)
+    back = sp.permute_tokens(y, dperm, inverse=True)
+    # strided in and out: (B, N, H, D) storage
+    xt = x.transpose(1, 2).contiguous().transpose(1, 2)
+    yt = torch.empty(2, N, 3, D, dtype=torch.bfloat16, device="cuda").transpose(1, 2)
+    sp.permute_tokens(xt, dperm, out=yt)
+    torch.cuda.synchronize()
+    want = oracle.permute_tokens(q, perm.numpy())
+    assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), want)
+    assert np.array_equal(back.view(torch.int16).cpu().numpy().view(np.uint16), q)
+    assert torch.equal(yt.contiguous().view(torch.int16), y.view(torch.int16))
+
+
+def test_permute_tokens_full_size(gpu_lib):
+    """The Wan2.1-14B 720p grid (40 heads, 75600 tokens): bit-exact cube reorder and restore."""
+    wl = synth.WORKLOADS[3]
+    q = synth.make_tensor(wl, "q", heads=[(0, h) for h in range(wl.H)])
+    perm = sp.token_permutation(0, wl.grid, "cube")
+    x = to_dev(q)
+    y = sp.permute_tokens(x, perm.cuda())
+    back = sp.permute_tokens(y, perm.cuda(), inverse=True)
+    torch.cuda.synchronize()
+    p = perm.numpy().astype(np.int64)
+    yh = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    for h in (0, 17, 39):
+        assert np.array_equal(yh[0, h], q[0, h][p])
+    assert torch.equal(back.view(torch.int16), x.view(torch.int16))
+
+
+@pytest.mark.parametrize("layout", ["cube", "morton"])
+def test_attention_in_cube_layout(gpu_lib, layout):
+    """Reorder, top-k attention, restore: equals the oracle run in the reordered space."""
+    small = synth.custom(1, 2, 226 + 4 * 10 * 12, 64, config_id=62, grid=(4, 10, 12), n_text=226, q_scale=0.125)
+    q, k, v = synth.make_qkv(small, seed=0)
+    perm = sp.token_permutation(226, (4, 10, 12), layout)
+    dperm = perm.cuda()
+    dq, dk, dv = (sp.permute_tokens(t, dperm) for t in _dev(q, k, v))
+    out_p, mask = sp.attn_topk(dq, dk, dv, topk=0.4, return_mask=True)
+    out = sp.permute_tokens(out_p, dperm, inverse=True)
+    m = mask.cpu().numpy()
+    p = perm.numpy()
+    qp, kp, vp = (oracle.permute_tokens(F64(t), p) for t in (q, k, v))
+    rep = oracle_mask_parity(lambda b, h: qp[b, h], lambda b, h: kp[b, h], 0.4, m)
+    assert rep["failures"] == 0, rep
+    ref = oracle.permute_tokens(oracle.masked_attention(qp, kp, vp, m), p, inverse=True)
+    print(assert_close(to_host_f64(out), ref, f"{layout} layout"), rep)
