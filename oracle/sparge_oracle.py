@@ -35,6 +35,13 @@ floor((last row of block i) / 64); it keeps ceil(topk * (J(i) + 1)) of them
 the kept blocks each row attends to its visible keys only. A row left with no
 visible kept key outputs zeros.
 
+CDF-threshold selection (the inference scripts' "cdfthreshd" mode, SpargeAttention
+Documentation, output-directory list; only the name and a value are given):
+per query block, the key blocks are taken in decreasing softmax probability
+(ties to the lower index) until their cumulative probability reaches the
+threshold tau in (0, 1]; tau = 1 keeps every candidate. The number kept varies
+from row to row.
+
 Token layouts (optional, around the whole method; Official repository for
 AB-Attention, "Optional cube layout"; Attention Mechanisms (LightX2V), Sol-Attn
 on Wan2.1, "Tuning and implementation"): video tokens of a T x H x W grid,
@@ -171,6 +178,50 @@ def predict_mask(q: np.ndarray, k: np.ndarray, topk: float, scale: float | None 
         p[..., i, :c] = row_softmax(s[..., i, :c])
         mask[..., i, :c] = select_topk(p[..., i, :c], int(kk[i]))
     return {"mask": mask, "logits": s, "probs": p, "qbar": qbar, "kbar": kbar, "k": kk, "cand": cand}
+
+
+def select_cdf(p: np.ndarray, tau: float) -> np.ndarray:
+    """0/1 mask keeping, per row, the fewest largest entries whose sum reaches tau
+    (entries in decreasing order, equal values by lower index); tau >= 1 keeps all."""
+    if not (tau > 0.0 and tau <= 1.0):
+        raise ValueError("tau must be in (0, 1]")
+    p = np.asarray(p, dtype=np.float64)
+    kb = p.shape[-1]
+    flat = p.reshape(-1, kb)
+    mask = np.zeros(flat.shape, dtype=np.uint8)
+    for r in range(flat.shape[0]):
+        order = np.argsort(-flat[r], kind="stable")
+        if tau >= 1.0:
+            mask[r, :] = 1
+            continue
+        total = 0.0
+        for j in order:
+            mask[r, j] = 1
+            total += flat[r, j]
+            if total >= tau:
+                break
+    return mask.reshape(p.shape)
+
+
+def predict_mask_cdf(q: np.ndarray, k: np.ndarray, tau: float, scale: float | None = None,
+                     causal: bool = False) -> dict:
+    """Pool -> score -> CDF-threshold selection (see select_cdf); with causal=True the
+    softmax and the selection of query block i run over key blocks 0 .. J(i) only."""
+    n, d = q.shape[-2], q.shape[-1]
+    scale = default_scale(d) if scale is None else float(scale)
+    qbar = pool_blocks(q, Q_BLOCK)
+    kbar = pool_blocks(k, K_BLOCK)
+    s = block_logits(qbar, kbar, scale)
+    n_qb, n_kb = qbar.shape[-2], kbar.shape[-2]
+    cand = np.array([causal_key_blocks(n, i) if causal else n_kb for i in range(n_qb)], dtype=np.int64)
+    p = np.zeros_like(s)
+    mask = np.zeros(s.shape, dtype=np.uint8)
+    for i in range(n_qb):
+        c = int(cand[i])
+        p[..., i, :c] = row_softmax(s[..., i, :c])
+        mask[..., i, :c] = select_cdf(p[..., i, :c], tau)
+    return {"mask": mask, "logits": s, "probs": p, "qbar": qbar, "kbar": kbar, "cand": cand,
+            "k": mask.sum(-1)}
 
 
 def selected_keys(mask_row: np.ndarray, n: int) -> np.ndarray:
@@ -365,3 +416,49 @@ def permute_tokens(x: np.ndarray, perm: np.ndarray, inverse: bool = False) -> np
     out[..., perm, :] = x
     return out
 
+
+def mask_parity_cdf(logits: np.ndarray, probs: np.ndarray, oracle_mask: np.ndarray,
+                    device_mask: np.ndarray, tau: float, band: float = 1e-5, mass_band: float = 1e-5,
+                    cand=None) -> dict:
+    """Compare a device CDF-threshold mask with the oracle's.
+
+    A row must equal the oracle's unless it sits at a float boundary. A differing
+    row is excused when, with k its own count: it keeps k candidates and no
+    other block; it keeps every candidate whose logit is at least t + band and
+    none at most t - band, t being the k-th largest candidate logit (a valid
+    top-k set up to near-ties); and the oracle's probabilities put the cut
+    there up to mass_band: the k best reach at least tau - mass_band and the
+    k - 1 best stay below tau + mass_band (tau = 1: k is every candidate).
+    """
+    s = np.asarray(logits, dtype=np.float64).reshape(-1, logits.shape[-1])
+    pr = np.asarray(probs, dtype=np.float64).reshape(s.shape)
+    om = np.asarray(oracle_mask).reshape(s.shape) != 0
+    dm = np.asarray(device_mask).reshape(s.shape) != 0
+    R, kb = s.shape
+    n_qb = logits.shape[-2]
+    cr = np.tile(np.broadcast_to(np.asarray(kb if cand is None else cand, dtype=np.int64), (n_qb,)), R // n_qb)
+    excused, differing, failing = 0, 0, []
+    for r in range(R):
+        if (om[r] == dm[r]).all():
+            continue
+        differing += 1
+        c = int(cr[r])
+        in_cand = np.arange(kb) < c
+        kd = int(dm[r].sum())
+        ok = 1 <= kd <= c and not (dm[r] & ~in_cand).any()
+        if ok:
+            cum = np.cumsum(-np.sort(-pr[r, :c]))
+            if tau >= 1.0:
+                ok = kd == c
+            else:
+                ok = cum[kd - 1] >= tau - mass_band and (kd == 1 or cum[kd - 2] < tau + mass_band)
+        if ok:
+            t = -np.sort(-np.where(in_cand, s[r], -np.inf))[kd - 1]
+            ok = (not (in_cand & (s[r] >= t + band) & ~dm[r]).any()
+                  and not (in_cand & (s[r] <= t - band) & dm[r]).any())
+        if ok:
+            excused += 1
+        elif len(failing) < 16:
+            failing.append(r)
+    return {"rows": int(R), "differing": differing, "excused": excused,
+            "failures": differing - excused, "failing_rows": failing}

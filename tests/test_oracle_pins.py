@@ -25,7 +25,7 @@ def _ns(**over):
              "block_logits", "row_softmax", "select_topk", "predict_mask", "selected_keys",
              "attend_rows", "masked_attention", "masked_attention_rows", "compact_mask", "mask_parity",
              "causal_key_blocks", "cube_permutation", "morton_code", "morton_permutation",
-             "permute_tokens"]
+             "permute_tokens", "select_cdf", "predict_mask_cdf", "mask_parity_cdf"]
     d = {n: getattr(real_oracle, n) for n in names}
     d.update(over)
     return types.SimpleNamespace(**d)
@@ -416,9 +416,57 @@ def pin_token_layouts(o):
     assert np.abs(o.permute_tokens(a, perm, inverse=True) - o.masked_attention(q, k, v, ones)).max() <= 1e-12
 
 
+def pin_cdf_select(o):
+    for row in _golden("cdf_select.txt"):
+        text = " ".join(row)
+        tau_s, p_s, keep_s = (x.strip() for x in text.split(":"))
+        p = np.array([float(x) for x in p_s.split()])
+        m = o.select_cdf(p[None], float(tau_s))[0]
+        assert np.flatnonzero(m).tolist() == [int(x) for x in keep_s.split()], text
+    rng = np.random.default_rng(13)
+    p = rng.dirichlet(np.full(40, 0.3), size=50)
+    prev = None
+    for tau in (0.05, 0.3, 0.6, 0.9, 0.999, 1.0):
+        m = o.select_cdf(p, tau)
+        for r in range(p.shape[0]):
+            kept = np.flatnonzero(m[r])
+            k = kept.size
+            # the kept set is the k largest (lower index on ties) ...
+            assert sorted(kept.tolist()) == sorted(np.argsort(-p[r], kind="stable")[:k].tolist())
+            # ... reaches tau, and one block fewer would not
+            srt = np.sort(p[r])[::-1]
+            if tau < 1.0:
+                assert srt[:k].sum() >= tau and (k == 1 or srt[:k - 1].sum() < tau)
+            else:
+                assert k == p.shape[1]
+        if prev is not None:
+            assert (m >= prev).all()          # nested as tau grows
+        prev = m
+    # the CDF mask equals the top-k mask of its own count
+    q, k = rng.standard_normal((1, 2, 500, 8)), rng.standard_normal((1, 2, 500, 8))
+    r = o.predict_mask_cdf(q, k, 0.6)
+    for h in range(2):
+        for i in range(r["mask"].shape[2]):
+            kk = int(r["mask"][0, h, i].sum())
+            assert (o.select_topk(r["probs"][0, h, i][None], kk)[0] == r["mask"][0, h, i]).all()
+    rc = o.predict_mask_cdf(q, k, 0.6, causal=True)
+    for i in range(rc["mask"].shape[2]):
+        assert not rc["mask"][..., i, rc["cand"][i]:].any()
+    # parity: exact rows, a cut shifted inside the mass band, and real mistakes
+    pr = np.array([[0.5, 0.3, 0.2]])
+    lg = np.log(pr)
+    tau = 0.8 + 1e-7
+    om = o.select_cdf(pr, tau)
+    assert om[0].tolist() == [1, 1, 1]
+    assert o.mask_parity_cdf(lg, pr, om, om, tau)["failures"] == 0
+    assert o.mask_parity_cdf(lg, pr, om, np.array([[1, 1, 0]]), tau)["failures"] == 0
+    assert o.mask_parity_cdf(lg, pr, om, np.array([[1, 0, 1]]), tau)["failures"] == 1
+    assert o.mask_parity_cdf(lg, pr, om, np.array([[1, 0, 0]]), tau)["failures"] == 1
+
+
 PINS = [pin_block_counts, pin_topk_count, pin_pool, pin_scores, pin_select, pin_predict,
         pin_predict_ties, pin_attention, pin_attention_closed_forms, pin_attention_rows,
-        pin_compact, pin_mask_parity, pin_causal_attention, pin_causal_predict, pin_token_layouts]
+        pin_compact, pin_mask_parity, pin_causal_attention, pin_causal_predict, pin_token_layouts, pin_cdf_select]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -536,6 +584,39 @@ def _broken_variants():
     def inverse_as_gather(x, perm, inverse=False):
         return np.asarray(x)[..., np.asarray(perm), :]
 
+    def cdf_strict(p, tau):
+        p = np.asarray(p, dtype=np.float64)
+        flat = p.reshape(-1, p.shape[-1])
+        m = np.zeros(flat.shape, dtype=np.uint8)
+        for r in range(flat.shape[0]):
+            total = 0.0
+            for j in np.argsort(-flat[r], kind="stable"):
+                m[r, j] = 1
+                total += flat[r, j]
+                if total > tau or tau >= 1.0 and m[r].all():
+                    break
+        return m.reshape(p.shape)
+
+    def _cdf_order(p, tau, ascending):
+        p = np.asarray(p, dtype=np.float64)
+        flat = p.reshape(-1, p.shape[-1])
+        m = np.zeros(flat.shape, dtype=np.uint8)
+        for r in range(flat.shape[0]):
+            total = 0.0
+            order = np.argsort(flat[r], kind="stable") if ascending else np.argsort(-flat[r], kind="stable")
+            for j in order:
+                m[r, j] = 1
+                total += flat[r, j]
+                if total >= tau:
+                    break
+        return m.reshape(p.shape)
+
+    def cdf_ascending(p, tau):
+        return _cdf_order(p, tau, ascending=True)
+
+    def parity_cdf_no_mass_band(lg, pr, om, dm, tau, band=1e-5, mass_band=1e-5, cand=None):
+        return o.mask_parity_cdf(lg, pr, om, dm, tau, band=band, mass_band=0.0, cand=cand)
+
     def causal_first_row(n, i):
         return (128 * i) // 64 + 1
 
@@ -560,6 +641,9 @@ def _broken_variants():
         "K used in place of V": dict(attend_rows=attend_transposed_v),
         "parity without the near-tie band": dict(mask_parity=parity_no_band),
         "causal row does not see its own key": dict(attend_rows=attend_causal_strict),
+        "CDF stops only past tau": dict(select_cdf=cdf_strict),
+        "CDF takes the smallest blocks first": dict(select_cdf=cdf_ascending),
+        "CDF parity without the mass band": dict(mask_parity_cdf=parity_cdf_no_mass_band),
         "cube order w-major inside a cube": dict(cube_permutation=cube_w_major),
         "cube order drops the partial edge cubes": dict(cube_permutation=cube_drops_partial),
         "Morton code with t as the lowest bit": dict(morton_code=morton_t_lowest),
