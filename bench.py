@@ -52,6 +52,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--causal", action="store_true", help="causal variant (is_causal=True)")
+    p.add_argument("--tau", type=float, default=None,
+                   help="CDF-threshold selection with this tau instead of top-k")
     p.add_argument("--layout", choices=["raster", "cube", "morton"], default="raster",
                    help="token order for the video grid: the step reorders Q, K, V, attends, restores O")
     p.add_argument("--recall-rows", type=int, default=0,
@@ -216,7 +218,8 @@ def main():
     dq, dk, dv = tod(q), tod(k), tod(v)
     out = torch.empty_like(dq)
     mask = torch.empty(sp.mask_shape(B, H, N), dtype=torch.uint8, device=dev)
-    ws = torch.empty(sp.workspace_bytes(B, H, N, D, topk), dtype=torch.uint8, device=dev)
+    cdf = args.tau is not None
+    ws = torch.empty(sp.workspace_bytes(B, H, N, D, 1.0 if cdf else topk), dtype=torch.uint8, device=dev)
     kk = sp.topk_count(mask.shape[-1], topk)
 
     causal = bool(args.causal)
@@ -232,6 +235,9 @@ def main():
         out_l = torch.empty_like(out)
 
     def step():
+        if cdf:
+            sp.attn_cdf(dq, dk, dv, tau=args.tau, out=out, workspace=ws, is_causal=causal)
+            return
         if layout == "raster":
             sp.attn_topk(dq, dk, dv, topk=topk, out=out, workspace=ws, is_causal=causal)
             return
@@ -244,7 +250,10 @@ def main():
     step()
     torch.cuda.synchronize()
     qbar, kbar = sp.pool_blocks(dq, 128), sp.pool_blocks(dk, 64)
-    mask_t, idx, cnt = sp.predict_mask(qbar, kbar, N, topk, is_causal=causal)
+    if cdf:
+        mask_t, idx, cnt = sp.predict_mask_cdf(qbar, kbar, N, args.tau, is_causal=causal)
+    else:
+        mask_t, idx, cnt = sp.predict_mask(qbar, kbar, N, topk, is_causal=causal)
     torch.cuda.synchronize()
     m = mask_t.cpu().numpy()
     eff = effective_flops(m, N, D, causal)
@@ -289,8 +298,11 @@ def main():
     log(f"attention kernel {attn_ms:.3f} ms (min {min(attn):.3f})")
     pool_q = kernel_durations_ms(lambda: sp.pool_blocks(dq, 128), 10)
     pool_k = kernel_durations_ms(lambda: sp.pool_blocks(dk, 64), 10)
-    pred = kernel_durations_ms(lambda: sp.predict_mask(qbar, kbar, N, topk, return_mask=True,
-                                                       is_causal=causal), 10)
+    if cdf:
+        pred = kernel_durations_ms(lambda: sp.predict_mask_cdf(qbar, kbar, N, args.tau, is_causal=causal), 10)
+    else:
+        pred = kernel_durations_ms(lambda: sp.predict_mask(qbar, kbar, N, topk, return_mask=True,
+                                                           is_causal=causal), 10)
     layout_info = {"name": layout}
     if layout != "raster":
         perm_ms = float(np.mean(kernel_durations_ms(lambda: sp.permute_tokens(rq, dperm, out=dq), 10)))
@@ -327,9 +339,10 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "H": H, "N": N, "D": D, "topk": topk, "k": kk,
-                   "causal": causal, "layout": layout,
+                   "causal": causal, "layout": layout, "tau": args.tau,
+                   "kept_fraction": float(m.mean()),
                    "n_qblocks": int(qb_), "n_kblocks": int(kb_), "seed": args.seed,
-                   "step": "sparge_attn_topk (pool Q, pool K, predict, attention)"},
+                   "step": ("sparge_attn_cdf" if cdf else "sparge_attn_topk") + " (pool Q, pool K, predict, attention)"},
         "dense_equiv_tflops": dense / (ms * 1e-3) / 1e12,
         "frac_peak_effective": eff / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "frac_peak_dense_equiv": dense / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
@@ -346,7 +359,7 @@ def main():
         "layout": layout_info,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": None if (causal or layout != "raster") else load_traffic(f"{wl.name}_topk{topk}"),
+                     "traffic": None if (causal or cdf or layout != "raster") else load_traffic(f"{wl.name}_topk{topk}"),
                      "kernel": f"attn_fwd_kernel<{D}> (sparge_attn_from_list)"},
     }
     if not args.no_cpu_baseline:

@@ -83,6 +83,9 @@ def load_library() -> ctypes.CDLL:
         "sparge_attn_topk": (ci, [vp, vp, vp, f64, vp, i64, i64, i64, i64, s3, s3, s3, s3, f32,
                                   ci, vp, vp, sz, vp]),
         "sparge_token_permutation": (ci, [i64, i64, i64, i64, ci, s3, vp]),
+        "sparge_predict_mask_cdf": (ci, [vp, vp, i64, i64, i64, i64, f64, f32, ci, vp, vp, vp, vp]),
+        "sparge_attn_cdf": (ci, [vp, vp, vp, f64, vp, i64, i64, i64, i64, s3, s3, s3, s3, f32,
+                                 ci, vp, vp, sz, vp]),
         "sparge_permute_tokens": (ci, [vp, vp, vp, i64, i64, i64, i64, s3, s3, ci, vp]),
     }
     for name, (res, args) in sig.items():
@@ -326,4 +329,43 @@ def permute_tokens(x: torch.Tensor, perm: torch.Tensor, inverse: bool = False, o
         _ptr(x), _ptr(perm), _ptr(out), B, H, N, D, _strides(x), _strides(out), int(bool(inverse)),
         _stream(x)))
     return out
+
+
+def predict_mask_cdf(qbar: torch.Tensor, kbar: torch.Tensor, N: int, tau: float, scale=None,
+                     return_mask: bool = True, is_causal: bool = False):
+    """CDF-threshold block selection from pooled means: per query block, key blocks in
+    decreasing probability until their sum reaches tau. Returns (mask_id or None,
+    kv_idx (B, H, Qb, Kb), kv_cnt)."""
+    if qbar.dtype != torch.float32 or kbar.dtype != torch.float32:
+        raise ValueError("qbar and kbar must be float32")
+    qbar, kbar = qbar.contiguous(), kbar.contiguous()
+    B, H, n_qb, D = qbar.shape
+    n_kb = kbar.shape[2]
+    if (n_qb, n_kb) != mask_shape(B, H, N)[2:] or kbar.shape[:2] != (B, H) or kbar.shape[3] != D:
+        raise ValueError("qbar / kbar shapes do not match N")
+    dev = qbar.device
+    mask = torch.empty((B, H, n_qb, n_kb), dtype=torch.uint8, device=dev) if return_mask else None
+    idx = torch.empty((B, H, n_qb, n_kb), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, H, n_qb), dtype=torch.int32, device=dev)
+    _check("sparge_predict_mask_cdf", load_library().sparge_predict_mask_cdf(
+        _ptr(qbar), _ptr(kbar), B, H, N, D, float(tau), _scale(scale, D), int(bool(is_causal)),
+        _ptr(mask), _ptr(idx), _ptr(cnt), _stream(qbar)))
+    return mask, idx, cnt
+
+
+def attn_cdf(q, k, v, tau=0.9, is_causal=False, scale=None, return_mask=False, out=None, workspace=None):
+    """Block-sparse attention with CDF-threshold selection (see predict_mask_cdf).
+
+    Returns out, or (out, mask_id) with return_mask=True.
+    """
+    q, k, v = _qkv(q, k, v)
+    B, H, N, D = q.shape
+    out = torch.empty_like(q) if out is None else out
+    mask = torch.empty(mask_shape(B, H, N), dtype=torch.uint8, device=q.device) if return_mask else None
+    ws = _workspace(q, B, H, N, D, 1.0, workspace)
+    _check("sparge_attn_cdf", load_library().sparge_attn_cdf(
+        _ptr(q), _ptr(k), _ptr(v), float(tau), _ptr(out), B, H, N, D, _strides(q), _strides(k),
+        _strides(v), _strides(out), _scale(scale, D), int(bool(is_causal)), _ptr(mask), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(q)))
+    return (out, mask) if return_mask else out
 

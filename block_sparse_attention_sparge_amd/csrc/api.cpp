@@ -414,4 +414,75 @@ int sparge_permute_tokens(const uint16_t* x, const int32_t* perm, uint16_t* out,
                                           static_cast<hipStream_t>(stream)));
 }
 
+int sparge_predict_mask_cdf(const float* qbar, const float* kbar, int64_t B, int64_t H, int64_t N,
+                            int64_t D, double tau, float scale, int is_causal, uint8_t* mask_id,
+                            int32_t* kv_idx, int32_t* kv_cnt, void* stream) {
+  if (!qbar || !kbar || !kv_idx || !kv_cnt) return SPARGE_ERR_NULL;
+  if (is_causal != 0 && is_causal != 1) return SPARGE_ERR_ARG;
+  if (int rc = check_shape(B, H, N, D)) return rc;
+  if (N > SPARGE_MAX_PREDICT_N) return SPARGE_ERR_SHAPE;
+  if (!(tau > 0.0 && tau <= 1.0)) return SPARGE_ERR_TOPK;
+  const size_t bh = static_cast<size_t>(B * H);
+  const size_t rows = bh * n_qblocks(N);
+  const Range in_q = range_bytes(qbar, rows * D * sizeof(float));
+  const Range in_k = range_bytes(kbar, bh * n_kblocks(N) * D * sizeof(float));
+  const Range outs[3] = {range_bytes(kv_idx, rows * n_kblocks(N) * sizeof(int32_t)),
+                         range_bytes(kv_cnt, rows * sizeof(int32_t)),
+                         mask_id ? range_bytes(mask_id, rows * n_kblocks(N)) : Range{0, 0}};
+  for (int i = 0; i < 3; ++i) {
+    if (overlap(outs[i], in_q) || overlap(outs[i], in_k)) return SPARGE_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return SPARGE_ERR_ALIAS;
+  }
+  return status_of(sparge::launch_predict_cdf(qbar, kbar, B * H, N, static_cast<int>(D), tau, is_causal,
+                                              resolve_scale(scale, D), mask_id, kv_idx, kv_cnt,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int sparge_attn_cdf(const uint16_t* q, const uint16_t* k, const uint16_t* v, double tau, uint16_t* out,
+                    int64_t B, int64_t H, int64_t N, int64_t D, const int64_t q_strides[3],
+                    const int64_t k_strides[3], const int64_t v_strides[3], const int64_t o_strides[3],
+                    float scale, int is_causal, uint8_t* mask_out, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (int rc = check_attn(q, k, v, out, B, H, N, D, q_strides, k_strides, v_strides, o_strides)) return rc;
+  if (is_causal != 0 && is_causal != 1) return SPARGE_ERR_ARG;
+  if (N > SPARGE_MAX_PREDICT_N) return SPARGE_ERR_SHAPE;
+  if (!(tau > 0.0 && tau <= 1.0)) return SPARGE_ERR_TOPK;
+  const int64_t kk = n_kblocks(N);   // a row may keep every block
+  const TopkWs w = topk_layout(B, H, N, D, kk);
+  if (!workspace || workspace_bytes < w.total || !aligned16(workspace)) return SPARGE_ERR_WORKSPACE;
+  const size_t rows = static_cast<size_t>(B * H * n_qblocks(N));
+  const Range rw = range_bytes(workspace, w.total);
+  const Range ro = range_bf16(out, B, H, N, D, o_strides);
+  const Range rq = range_bf16(q, B, H, N, D, q_strides);
+  const Range rk = range_bf16(k, B, H, N, D, k_strides);
+  const Range rv = range_bf16(v, B, H, N, D, v_strides);
+  if (overlap(rw, ro) || overlap(rw, rq) || overlap(rw, rk) || overlap(rw, rv)) return SPARGE_ERR_ALIAS;
+  if (mask_out) {
+    const Range rm = range_bytes(mask_out, rows * n_kblocks(N));
+    if (overlap(rm, ro) || overlap(rm, rw) || overlap(rm, rq) || overlap(rm, rk) || overlap(rm, rv))
+      return SPARGE_ERR_ALIAS;
+  }
+  const float sc = resolve_scale(scale, D);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* qbar = reinterpret_cast<float*>(ws + w.qbar);
+  float* kbar = reinterpret_cast<float*>(ws + w.kbar);
+  int32_t* idx = reinterpret_cast<int32_t*>(ws + w.idx);
+  int32_t* cnt = reinterpret_cast<int32_t*>(ws + w.cnt);
+  const Strides qs{q_strides[0], q_strides[1], q_strides[2]};
+  const Strides ks{k_strides[0], k_strides[1], k_strides[2]};
+  if (int rc = status_of(sparge::launch_pool(q, B, H, N, static_cast<int>(D), qs, SPARGE_Q_BLOCK, qbar, st))) return rc;
+  if (int rc = status_of(sparge::launch_pool(k, B, H, N, static_cast<int>(D), ks, SPARGE_K_BLOCK, kbar, st))) return rc;
+  if (int rc = status_of(sparge::launch_predict_cdf(qbar, kbar, B * H, N, static_cast<int>(D), tau, is_causal,
+                                                    sc, mask_out, idx, cnt, st)))
+    return rc;
+  sparge::AttnArgs a = attn_args(q, k, v, out, B, H, N, D, q_strides, k_strides, v_strides, o_strides, sc);
+  a.kv_idx = idx;
+  a.kv_cnt = cnt;
+  a.ld_idx = kk;
+  a.causal = is_causal;
+  return status_of(sparge::launch_attention(a, st));
+}
+
 }  // extern "C"

@@ -27,6 +27,13 @@ hipError_t launch_predict(const float* qbar, const float* kbar, int64_t BH, int6
                           int64_t k, double topk, int causal, float scale, uint8_t* mask,
                           int32_t* kv_idx, int32_t* kv_cnt, hipStream_t stream);
 
+// CDF-threshold selection: each row keeps its blocks in decreasing softmax
+// probability until the running sum reaches tau (tau >= 1: every candidate);
+// kv_idx rows are N_KB long, kv_cnt receives each row's count.
+hipError_t launch_predict_cdf(const float* qbar, const float* kbar, int64_t BH, int64_t N, int D,
+                              double tau, int causal, float scale, uint8_t* mask, int32_t* kv_idx,
+                              int32_t* kv_cnt, hipStream_t stream);
+
 hipError_t launch_compact(const uint8_t* mask, int64_t rows, int64_t n_kb, int32_t* kv_idx,
                           int32_t* kv_cnt, hipStream_t stream);
 

@@ -12,6 +12,13 @@
 // rows may see, and keeps ceil(topk * (J(i) + 1)) of them (the host's rounding
 // rule, evaluated here in double precision).
 //
+// CDF-threshold variant (the "cdfthreshd" mode of the inference scripts, only
+// named on the pages): each row keeps its key blocks in decreasing softmax
+// probability until their running sum reaches tau. The probabilities are taken
+// in fp32 against the row max and turned into 31-bit fixed-point weights, whose
+// integer sums are exact in any order; the cut is found by the same radix
+// select with weight histograms instead of counts.
+//
 // One workgroup (4 wavefronts) takes R query blocks of one head. Scores for
 // all R rows live in LDS. Selection is an exact radix select on order-preserving
 // 32-bit keys (4 passes of 8 bits, LDS histograms, wavefront prefix sums), one
@@ -46,23 +53,13 @@ __device__ __forceinline__ uint32_t count_below(uint64_t m) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
 }
 
+// Stages the R pooled query rows of a group (zeros past the last query block)
+// and writes their fp32 scores against every key block of the head to sc.
 template <int D, int R>
-__global__ __launch_bounds__(kThreads) void predict_kernel(
-    const float* __restrict__ qbar, const float* __restrict__ kbar, int64_t N, int64_t n_qb,
-    int64_t n_kb, int64_t n_groups, int64_t k, double topk, int causal, float scale,
-    uint8_t* __restrict__ mask, int32_t* __restrict__ kv_idx, int32_t* __restrict__ kv_cnt) {
-  extern __shared__ float4 smem4[];
-  float* q_lds = reinterpret_cast<float*>(smem4);          // [R][D]
-  float* sc = q_lds + R * D;                               // [R][n_kb]
-  uint32_t* hist = reinterpret_cast<uint32_t*>(sc + R * n_kb);   // [kWaves][256]
-
-  const int64_t bh = blockIdx.x / n_groups;
-  const int64_t row0 = (blockIdx.x - bh * n_groups) * R;   // first query block of this group
+__device__ __forceinline__ void pooled_scores(const float* __restrict__ qbar, const float* __restrict__ kbar,
+                                              int64_t bh, int64_t row0, int64_t n_qb, int64_t n_kb,
+                                              float scale, float* q_lds, float* sc) {
   const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = t >> 6;
-
-  // Stage the R pooled query rows (zeros past the last query block).
   for (int e = t; e < R * D; e += kThreads) {
     const int r = e / D;
     const int64_t qi = row0 + r;
@@ -93,6 +90,32 @@ __global__ __launch_bounds__(kThreads) void predict_kernel(
     for (int r = 0; r < R; ++r) sc[r * n_kb + j] = scale * acc[r];
   }
   __syncthreads();
+}
+
+// Candidate key blocks of query block qi: all of them, or with causal masking
+// the blocks 0 .. (last row of the block) / 64.
+__device__ __forceinline__ int64_t candidates(int causal, int64_t qi, int64_t N, int64_t n_kb) {
+  if (!causal) return n_kb;
+  const int64_t last_row = (qi + 1) * kQBlock < N ? (qi + 1) * kQBlock - 1 : N - 1;
+  return last_row / kKBlock + 1;
+}
+
+template <int D, int R>
+__global__ __launch_bounds__(kThreads) void predict_kernel(
+    const float* __restrict__ qbar, const float* __restrict__ kbar, int64_t N, int64_t n_qb,
+    int64_t n_kb, int64_t n_groups, int64_t k, double topk, int causal, float scale,
+    uint8_t* __restrict__ mask, int32_t* __restrict__ kv_idx, int32_t* __restrict__ kv_cnt) {
+  extern __shared__ float4 smem4[];
+  float* q_lds = reinterpret_cast<float*>(smem4);          // [R][D]
+  float* sc = q_lds + R * D;                               // [R][n_kb]
+  uint32_t* hist = reinterpret_cast<uint32_t*>(sc + R * n_kb);   // [kWaves][256]
+
+  const int64_t bh = blockIdx.x / n_groups;
+  const int64_t row0 = (blockIdx.x - bh * n_groups) * R;   // first query block of this group
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  pooled_scores<D, R>(qbar, kbar, bh, row0, n_qb, n_kb, scale, q_lds, sc);
 
   // Selection: wavefront `wave` takes rows wave, wave + 4, ...; every wavefront
   // runs the same number of rounds so the block-wide barriers stay uniform.
@@ -106,8 +129,7 @@ __global__ __launch_bounds__(kThreads) void predict_kernel(
     // candidates [0, n_cand) and the number kept, k_row
     int64_t n_cand = n_kb, k_row = k;
     if (causal && active) {
-      const int64_t last_row = (qi + 1) * kQBlock < N ? (qi + 1) * kQBlock - 1 : N - 1;
-      n_cand = last_row / kKBlock + 1;
+      n_cand = candidates(causal, qi, N, n_kb);
       k_row = topk_count_dev(n_cand, topk);
     }
 
@@ -180,6 +202,151 @@ __global__ __launch_bounds__(kThreads) void predict_kernel(
   }
 }
 
+// Wavefront reductions and scans (every lane ends with the same result).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+  return __shfl(x, 0, 64);
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return __shfl(x, 0, 64);   // lanes may round differently: take lane 0's
+}
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+// Sum of x over the lanes below this one.
+__device__ __forceinline__ uint64_t wave_exclusive_u64(uint64_t x, int lane) {
+  uint64_t incl = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint64_t o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  return incl - x;
+}
+
+constexpr float kLog2eF = 1.4426950408889634f;
+constexpr float kFixedOne = 2147483648.0f;   // weights in units of 2^-31
+
+template <int D, int R>
+__global__ __launch_bounds__(kThreads) void predict_cdf_kernel(
+    const float* __restrict__ qbar, const float* __restrict__ kbar, int64_t N, int64_t n_qb,
+    int64_t n_kb, int64_t n_groups, double tau, int causal, float scale,
+    uint8_t* __restrict__ mask, int32_t* __restrict__ kv_idx, int32_t* __restrict__ kv_cnt) {
+  extern __shared__ float4 smem4[];
+  float* q_lds = reinterpret_cast<float*>(smem4);          // [R][D]
+  float* sc = q_lds + R * D;                               // [R][n_kb]
+  // [kWaves][256] 64-bit weight histograms, 8-byte aligned after the scores
+  uint64_t* hist = reinterpret_cast<uint64_t*>(q_lds + ((R * D + R * n_kb + 1) & ~int64_t(1)));
+
+  const int64_t bh = blockIdx.x / n_groups;
+  const int64_t row0 = (blockIdx.x - bh * n_groups) * R;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  pooled_scores<D, R>(qbar, kbar, bh, row0, n_qb, n_kb, scale, q_lds, sc);
+
+  uint64_t* h = hist + wave * 256;
+  constexpr int kRounds = (R + kWaves - 1) / kWaves;
+  for (int round = 0; round < kRounds; ++round) {
+    const int r = wave + round * kWaves;
+    const int64_t qi = row0 + r;
+    const bool active = (r < R) && (qi < n_qb);
+    const float* srow = sc + (r < R ? r : 0) * n_kb;
+    const int64_t n_cand = active ? candidates(causal, qi, N, n_kb) : 0;
+
+    // softmax over the candidates, as fixed-point weights
+    float mx = -INFINITY;
+    for (int64_t j = lane; j < n_cand; j += 64) mx = fmaxf(mx, srow[j]);
+    mx = wave_max(mx);
+    float z = 0.f;
+    for (int64_t j = lane; j < n_cand; j += 64) z += __builtin_amdgcn_exp2f((srow[j] - mx) * kLog2eF);
+    z = wave_sum(z);
+    const float inv_z = (z > 0.f) ? 1.f / z : 0.f;
+    auto weight = [&](int64_t j) -> uint64_t {
+      const float pj = __builtin_amdgcn_exp2f((srow[j] - mx) * kLog2eF) * inv_z;
+      const float f = fminf(pj * kFixedOne + 0.5f, kFixedOne);
+      return static_cast<uint64_t>(f);
+    };
+    uint64_t w_all = 0;
+    for (int64_t j = lane; j < n_cand; j += 64) w_all += weight(j);
+    w_all = wave_sum_u64(w_all);
+    const bool keep_all = tau >= 1.0;
+    uint64_t rem = keep_all ? w_all : static_cast<uint64_t>(__builtin_ceil(tau * static_cast<double>(w_all)));
+    if (rem < 1) rem = 1;
+
+    uint32_t prefix = 0, prefix_mask = 0;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) h[lane * 4 + q] = 0u;
+      __syncthreads();
+      if (!keep_all) {
+        for (int64_t j = lane; j < n_cand; j += 64) {
+          const uint32_t u = order_key(srow[j]);
+          if ((u & prefix_mask) == prefix) atomicAdd(&h[(u >> shift) & 255u], weight(j));
+        }
+      }
+      __syncthreads();
+      // lane L owns bins 4L..4L+3; above(d) = weight of the candidates with a larger digit
+      const uint64_t c0 = h[lane * 4 + 0], c1 = h[lane * 4 + 1], c2 = h[lane * 4 + 2], c3 = h[lane * 4 + 3];
+      const uint64_t mine = c0 + c1 + c2 + c3;
+      uint64_t suf = mine;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint64_t o = __shfl_down(suf, off, 64);
+        if (lane + off < 64) suf += o;
+      }
+      const uint64_t above3 = suf - mine;
+      const uint64_t above2 = above3 + c3, above1 = above2 + c2, above0 = above1 + c1;
+      int digit = -1;
+      uint64_t above = 0;
+      if (c3 && above3 < rem && rem <= above3 + c3) { digit = lane * 4 + 3; above = above3; }
+      else if (c2 && above2 < rem && rem <= above2 + c2) { digit = lane * 4 + 2; above = above2; }
+      else if (c1 && above1 < rem && rem <= above1 + c1) { digit = lane * 4 + 1; above = above1; }
+      else if (c0 && above0 < rem && rem <= above0 + c0) { digit = lane * 4 + 0; above = above0; }
+      const uint64_t who = __ballot(digit >= 0);
+      const int src = who ? __builtin_ctzll(who) : 0;
+      digit = __shfl(digit, src, 64);
+      const uint64_t above_sel = __shfl(above, src, 64);
+      prefix |= static_cast<uint32_t>(digit < 0 ? 0 : digit) << shift;
+      prefix_mask |= 255u << shift;
+      if (digit >= 0) rem -= above_sel;
+    }
+
+    // keep every key above the cut and, in index order, the keys equal to it
+    // until their weight reaches what is still missing
+    if (active) {
+      const uint32_t thr = prefix;
+      const int64_t row = bh * n_qb + qi;
+      int32_t* out_idx = kv_idx + row * n_kb;
+      uint8_t* out_mask = mask ? mask + row * n_kb : nullptr;
+      int64_t base = 0;
+      uint64_t eq_before = 0;
+      for (int64_t j0 = 0; j0 < n_kb; j0 += 64) {
+        const int64_t j = j0 + lane;
+        const bool valid = j < n_cand;
+        const uint32_t u = valid ? order_key(srow[j]) : 0u;
+        const bool is_eq = valid && !keep_all && u == thr;
+        const uint64_t w_eq = is_eq ? weight(j) : 0u;
+        const uint64_t eq_cum = eq_before + wave_exclusive_u64(w_eq, lane);
+        const bool sel = valid && (keep_all || u > thr || (is_eq && eq_cum < rem));
+        const uint64_t sel_b = __ballot(sel);
+        const int64_t pos = base + count_below(sel_b);
+        if (sel) out_idx[pos] = static_cast<int32_t>(j);
+        if (out_mask && j < n_kb) out_mask[j] = sel ? 1 : 0;
+        base += __popcll(sel_b);
+        eq_before += wave_sum_u64(w_eq);
+      }
+      if (lane == 0) kv_cnt[row] = static_cast<int32_t>(base);
+    }
+  }
+}
+
 template <int D, int R>
 hipError_t launch_predict_t(const float* qbar, const float* kbar, int64_t BH, int64_t N, int64_t n_qb,
                             int64_t n_kb, int64_t k, double topk, int causal, float scale,
@@ -207,7 +374,44 @@ hipError_t launch_predict_d(const float* qbar, const float* kbar, int64_t BH, in
   return launch_predict_t<D, 1>(qbar, kbar, BH, N, n_qb, n_kb, k, topk, causal, scale, mask, kv_idx, kv_cnt, stream);
 }
 
+template <int D, int R>
+hipError_t launch_cdf_t(const float* qbar, const float* kbar, int64_t BH, int64_t N, int64_t n_qb,
+                        int64_t n_kb, double tau, int causal, float scale, uint8_t* mask,
+                        int32_t* kv_idx, int32_t* kv_cnt, hipStream_t stream) {
+  const int64_t n_groups = (n_qb + R - 1) / R;
+  const size_t lds = sizeof(float) * ((R * D + R * n_kb + 1) & ~int64_t(1)) + sizeof(uint64_t) * kWaves * 256;
+  void* args[] = {(void*)&qbar, (void*)&kbar, (void*)&N, (void*)&n_qb, (void*)&n_kb,
+                  (void*)&n_groups, (void*)&tau, (void*)&causal, (void*)&scale,
+                  (void*)&mask, (void*)&kv_idx, (void*)&kv_cnt};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&predict_cdf_kernel<D, R>),
+                         dim3(static_cast<uint32_t>(BH * n_groups)), dim3(kThreads), args, lds,
+                         stream);
+}
+
+template <int D>
+hipError_t launch_cdf_d(const float* qbar, const float* kbar, int64_t BH, int64_t N, int64_t n_qb,
+                        int64_t n_kb, double tau, int causal, float scale, uint8_t* mask,
+                        int32_t* kv_idx, int32_t* kv_cnt, hipStream_t stream) {
+  if (n_kb <= 1536)
+    return launch_cdf_t<D, 8>(qbar, kbar, BH, N, n_qb, n_kb, tau, causal, scale, mask, kv_idx, kv_cnt, stream);
+  if (n_kb <= 3072)
+    return launch_cdf_t<D, 4>(qbar, kbar, BH, N, n_qb, n_kb, tau, causal, scale, mask, kv_idx, kv_cnt, stream);
+  if (n_kb <= 6144)
+    return launch_cdf_t<D, 2>(qbar, kbar, BH, N, n_qb, n_kb, tau, causal, scale, mask, kv_idx, kv_cnt, stream);
+  return launch_cdf_t<D, 1>(qbar, kbar, BH, N, n_qb, n_kb, tau, causal, scale, mask, kv_idx, kv_cnt, stream);
+}
+
 }  // namespace
+
+hipError_t launch_predict_cdf(const float* qbar, const float* kbar, int64_t BH, int64_t N, int D,
+                              double tau, int causal, float scale, uint8_t* mask, int32_t* kv_idx,
+                              int32_t* kv_cnt, hipStream_t stream) {
+  const int64_t n_qb = (N + kQBlock - 1) / kQBlock;
+  const int64_t n_kb = (N + kKBlock - 1) / kKBlock;
+  if (D == 128)
+    return launch_cdf_d<128>(qbar, kbar, BH, N, n_qb, n_kb, tau, causal, scale, mask, kv_idx, kv_cnt, stream);
+  return launch_cdf_d<64>(qbar, kbar, BH, N, n_qb, n_kb, tau, causal, scale, mask, kv_idx, kv_cnt, stream);
+}
 
 hipError_t launch_predict(const float* qbar, const float* kbar, int64_t BH, int64_t N, int D,
                           int64_t k, double topk, int causal, float scale, uint8_t* mask,

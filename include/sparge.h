@@ -182,6 +182,33 @@ int sparge_attn_topk(const uint16_t *q, const uint16_t *k, const uint16_t *v, do
                      int is_causal, uint8_t *mask_out, void *workspace, size_t workspace_bytes,
                      void *stream);
 
+/* CDF-threshold selection (the inference scripts' "cdfthreshd" mode, SpargeAttention
+ * Documentation, output-directory list; the pages give only the name and a
+ * value, this is the library's reading): each query block keeps its key blocks
+ * in decreasing softmax probability (ties to the lower index) until their
+ * cumulative probability reaches tau in (0, 1]; tau = 1 keeps every candidate.
+ * The count varies from row to row. Probabilities are fp32 against the row
+ * max, summed as exact 31-bit fixed-point weights, so the result is
+ * deterministic. Causal candidates as for sparge_predict_mask.
+ *   kv_idx   (B, H, N_QB, N_KB) int32 contiguous; row r lists kv_cnt[r] ids ascending.
+ *   kv_cnt   (B, H, N_QB) int32.
+ * Other arguments as sparge_predict_mask (tau in place of topk; a tau outside
+ * (0, 1] is SPARGE_ERR_TOPK).
+ * Errors: NULL, SHAPE (also N > SPARGE_MAX_PREDICT_N), TOPK, ARG, ALIAS, LAUNCH. */
+int sparge_predict_mask_cdf(const float *qbar, const float *kbar, int64_t B, int64_t H, int64_t N,
+                            int64_t D, double tau, float scale, int is_causal, uint8_t *mask_id,
+                            int32_t *kv_idx, int32_t *kv_cnt, void *stream);
+
+/* Pool, CDF-threshold selection and attention back to back (as sparge_attn_topk).
+ *   workspace   device buffer of at least sparge_workspace_bytes(B, H, N, D, 1.0)
+ *               (room for every row to keep every block).
+ * Errors: NULL, SHAPE, TOPK (tau), STRIDE, ALIAS, ARG, WORKSPACE, LAUNCH. */
+int sparge_attn_cdf(const uint16_t *q, const uint16_t *k, const uint16_t *v, double tau, uint16_t *out,
+                    int64_t B, int64_t H, int64_t N, int64_t D, const int64_t q_strides[3],
+                    const int64_t k_strides[3], const int64_t v_strides[3], const int64_t o_strides[3],
+                    float scale, int is_causal, uint8_t *mask_out, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
 /* Token layouts for sparge_token_permutation. */
 #define SPARGE_LAYOUT_RASTER 0   /* identity */
 #define SPARGE_LAYOUT_CUBE 1     /* video tokens cube by cube */

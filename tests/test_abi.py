@@ -151,6 +151,25 @@ def test_pool_predict_compact_errors(lib):
                                      5, None) == ARG
 
 
+def test_cdf_errors(lib):
+    st = contiguous(2, 256, 64)
+    assert lib.sparge_predict_mask_cdf(None, Bp, 1, 2, 256, 64, 0.5, 0.0, 0, None, C, O, None) == NULL
+    assert lib.sparge_predict_mask_cdf(A, Bp, 1, 2, 256, 64, 0.0, 0.0, 0, None, C, O, None) == TOPK
+    assert lib.sparge_predict_mask_cdf(A, Bp, 1, 2, 256, 64, 1.5, 0.0, 0, None, C, O, None) == TOPK
+    assert lib.sparge_predict_mask_cdf(A, Bp, 1, 2, 256, 64, 0.5, 0.0, 2, None, C, O, None) == ARG
+    assert lib.sparge_predict_mask_cdf(A, Bp, 1, 2, 786433, 64, 0.5, 0.0, 0, None, C, O, None) == SHAPE
+    assert lib.sparge_predict_mask_cdf(A, Bp, 1, 2, 256, 64, 0.5, 0.0, 0, None, A + 4, O, None) == ALIAS
+    need = sp.workspace_bytes(1, 2, 256, 64, 1.0)
+    call = lambda tau=0.5, causal=0, ws=W, wsb=need, out=O: lib.sparge_attn_cdf(
+        A, Bp, C, tau, out, 1, 2, 256, 64, st, st, st, st, 0.0, causal, None, ws, wsb, None)
+    assert call(out=None) == NULL
+    assert call(tau=float("nan")) == TOPK
+    assert call(causal=7) == ARG
+    assert call(ws=0) == WORKSPACE
+    assert call(wsb=need - 16) == WORKSPACE
+    assert call(ws=O + 64) == ALIAS
+
+
 def test_permute_tokens_errors(lib):
     st = contiguous(2, 256, 64)
     assert lib.sparge_permute_tokens(None, Bp, O, 1, 2, 256, 64, st, st, 0, None) == NULL

@@ -419,3 +419,76 @@ def test_attention_in_cube_layout(gpu_lib, layout):
     assert rep["failures"] == 0, rep
     ref = oracle.permute_tokens(oracle.masked_attention(qp, kp, vp, m), p, inverse=True)
     print(assert_close(to_host_f64(out), ref, f"{layout} layout"), rep)
+
+
+# ------------------------------------------------------------ CDF-threshold selection
+
+
+def _cdf_parity(q, k, tau, m, scale=None, causal=False):
+    B, H = m.shape[:2]
+    tot = {"rows": 0, "differing": 0, "excused": 0, "failures": 0}
+    for b in range(B):
+        for h in range(H):
+            pr = oracle.predict_mask_cdf(F64(q[b, h])[None, None], F64(k[b, h])[None, None], tau, scale,
+                                         causal=causal)
+            rep = oracle.mask_parity_cdf(pr["logits"], pr["probs"], pr["mask"], m[b, h][None, None], tau,
+                                         cand=pr["cand"])
+            for key in tot:
+                tot[key] += rep[key]
+    return tot
+
+
+@pytest.mark.parametrize("B,H,N,D", SMALL)
+@pytest.mark.parametrize("tau", [0.3, 0.7, 0.95, 1.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_cdf_predict(gpu_lib, B, H, N, D, tau, causal):
+    # a large logit scale makes the block probabilities uneven, so tau matters
+    q, k, v = rand_qkv(B, H, N, D, seed=17 * N + D)
+    scale = 40.0
+    mask, idx, cnt = sp.predict_mask_cdf(sp.pool_blocks(to_dev(q), 128), sp.pool_blocks(to_dev(k), 64), N, tau,
+                                         scale=scale, is_causal=causal)
+    m, idx, cnt = mask.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy()
+    rep = _cdf_parity(q, k, tau, m, scale, causal)
+    print(rep, "kept fraction", m.mean())
+    assert rep["failures"] == 0, rep
+    assert (cnt == m.sum(-1)).all()
+    for b in range(B):
+        for h in range(H):
+            for i in range(m.shape[2]):
+                assert idx[b, h, i, : cnt[b, h, i]].tolist() == np.flatnonzero(m[b, h, i]).tolist()
+    if tau == 1.0:
+        cand = np.array([oracle.causal_key_blocks(N, i) if causal else m.shape[3] for i in range(m.shape[2])])
+        assert (cnt == cand[None, None]).all()
+
+
+@pytest.mark.parametrize("B,H,N,D", SMALL[:3])
+@pytest.mark.parametrize("causal", [False, True])
+def test_attn_cdf(gpu_lib, B, H, N, D, causal):
+    q, k, v = rand_qkv(B, H, N, D, seed=19 * N + D)
+    out, mask = sp.attn_cdf(*_dev(q, k, v), tau=0.6, scale=0.5, is_causal=causal, return_mask=True)
+    m = mask.cpu().numpy()
+    ref = oracle.masked_attention(F64(q), F64(k), F64(v), m, scale=0.5, causal=causal)
+    print(assert_close(to_host_f64(out), ref, f"cdf {B, H, N, D} causal={causal}"), "kept", m.mean())
+    rep = _cdf_parity(q, k, 0.6, m, 0.5, causal)
+    assert rep["failures"] == 0, rep
+
+
+@pytest.mark.parametrize("cfg,tau", [(1, 0.9), (2, 0.8)], ids=["cfg1-tau0.9", "cfg2-tau0.8"])
+def test_cdf_workload_parity(gpu_lib, cfg, tau):
+    """CDF selection at a workload's full size: every mask row, sampled output rows."""
+    wl = synth.WORKLOADS[cfg]
+    print(f"cdf workload {wl.describe()} tau={tau}", flush=True)
+    q, k, v = synth.make_qkv(wl, seed=0)
+    out, mask = sp.attn_cdf(*_dev(q, k, v), tau=tau, return_mask=True)
+    torch.cuda.synchronize()
+    m = mask.cpu().numpy()
+    rep = _cdf_parity(q, k, tau, m)
+    print("mask parity", rep, "kept fraction", float(m.mean()), flush=True)
+    assert rep["failures"] == 0
+    rng = np.random.default_rng(200 + cfg)
+    outs = out.view(torch.int16)
+    for b, h in sorted({(0, 0), (wl.B - 1, wl.H - 1)}):
+        rows = _sample_rows(wl.N, rng)
+        got = synth.bf16_bits_to_f64(outs[b, h, torch.from_numpy(rows).cuda()].cpu().numpy().view(np.uint16))
+        ref = oracle.masked_attention_rows(F64(q[b, h]), F64(k[b, h]), F64(v[b, h]), m[b, h], rows)
+        print(assert_close(got, ref, f"cdf cfg{cfg} head {(b, h)}"), flush=True)
