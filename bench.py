@@ -318,6 +318,17 @@ def main():
         layout_info["recall"] = recall_share(qh, kh, m[0, 0], rows, 1.0 / np.sqrt(D), causal)
     bsa = kernel_durations_ms(lambda: sp.block_sparse_attn(dq, dk, dv, mask_id=mask_t, out=out,
                                                            is_causal=causal), 5)
+    # plan reuse: the kept-block lists parked in pinned host memory between calls and brought back
+    h_idx = torch.empty(idx.shape, dtype=idx.dtype, pin_memory=True)
+    h_cnt = torch.empty(cnt.shape, dtype=cnt.dtype, pin_memory=True)
+
+    def roundtrip():
+        h_idx.copy_(idx, non_blocking=True)
+        h_cnt.copy_(cnt, non_blocking=True)
+        idx.copy_(h_idx, non_blocking=True)
+        cnt.copy_(h_cnt, non_blocking=True)
+    plan_rt = kernel_durations_ms(roundtrip, 5)
+    plan_bytes = idx.numel() * 4 + cnt.numel() * 4
 
     qb_, kb_ = m.shape[-2:]
     pool_bytes_q = B * H * N * D * 2 + B * H * qb_ * D * 4
@@ -351,6 +362,9 @@ def main():
                              "effective_tflops": achieved,
                              "dense_equiv_tflops": dense / (attn_ms * 1e-3) / 1e12},
         "block_sparse_attn_ms": float(np.mean(bsa)),
+        "plan_reuse": {"apply_ms": attn_ms, "predict_and_apply_ms": ms,
+                       "lists_bytes": int(plan_bytes),
+                       "pinned_roundtrip_ms": float(np.mean(plan_rt))},
         "pool_q": {"ms": float(np.mean(pool_q)), "gbs": pool_bytes_q / (np.mean(pool_q) * 1e-3) / 1e9},
         "pool_k": {"ms": float(np.mean(pool_k)), "gbs": pool_bytes_k / (np.mean(pool_k) * 1e-3) / 1e9},
         "predict": {"ms": float(np.mean(pred)),
