@@ -374,7 +374,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": None if (causal or cdf or layout != "raster") else load_traffic(f"{wl.name}_topk{topk}"),
-                     "kernel": f"attn_fwd_kernel<{D}> (sparge_attn_from_list)"},
+                     "kernel": f"attn_fwd_kernel<{D}, {str(causal).lower()}> (sparge_attn_from_list)"},
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle sample")

@@ -100,7 +100,6 @@ struct Params {
   int64_t per_xcd;     // query blocks per XCD slice of a head
   Strides qs, ks, vs, os;
   float c;             // scale * log2(e)
-  int causal;          // 1: row r sees keys c <= r only
 };
 
 // Row of the K tile that feeds A-operand row m, chosen so that accumulator
@@ -135,7 +134,7 @@ __device__ __forceinline__ uint4 load16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
-template <int D>
+template <int D, bool kCausal>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   using C = Cfg<D>;
   // Four separate LDS objects (not one array) so that waits for the loads
@@ -153,7 +152,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   // short lists fill in at the end instead of one XCD carrying the long ones.
   const int64_t wid = blockIdx.x;
   int64_t bh, qb;
-  if (!p.causal) {
+  if constexpr (!kCausal) {
     const int64_t xcd = wid % kNumXcd;
     const int64_t it = wid / kNumXcd;
     bh = it / p.per_xcd;
@@ -284,11 +283,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   // sequence end or across the block's diagonal need the per-key test.
   auto mask_keys = [&](int64_t j, f32x16& s0, f32x16& s1) {
     const int64_t k0 = j * kKBlock;
-    if (k0 + kKBlock > p.N || (p.causal && k0 + kKBlock - 1 > qb * kQBlock)) {
+    if (k0 + kKBlock > p.N || (kCausal && k0 + kKBlock - 1 > qb * kQBlock)) {
       // keys k0 + lim and later are masked; register i of this lane holds key
       // 8g + i (i < 8) or 8g + 16 + (i - 8)
       int64_t lim64 = p.N - k0;
-      if (p.causal && qrow - k0 + 1 < lim64) lim64 = qrow - k0 + 1;
+      if (kCausal && qrow - k0 + 1 < lim64) lim64 = qrow - k0 + 1;
       const int lim = static_cast<int>(lim64 < 0 ? 0 : (lim64 > kKBlock ? kKBlock : lim64)) - 8 * g;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -459,10 +458,11 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   p.per_xcd = (p.n_qb + kNumXcd - 1) / kNumXcd;
   p.qs = a.qs; p.ks = a.ks; p.vs = a.vs; p.os = a.os;
   p.c = a.scale * kLog2e;
-  p.causal = a.causal;
   const int64_t grid = a.B * a.H * kNumXcd * p.per_xcd;
   void* args[] = {(void*)&p};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<D>),
+  const void* fn = a.causal ? reinterpret_cast<const void*>(&attn_fwd_kernel<D, true>)
+                           : reinterpret_cast<const void*>(&attn_fwd_kernel<D, false>);
+  return hipLaunchKernel(fn,
                          dim3(static_cast<uint32_t>(grid)), dim3(256), args, 0, stream);
 }
 
