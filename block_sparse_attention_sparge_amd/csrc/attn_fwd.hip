@@ -396,6 +396,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
       const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vh, more ? j1 : p.n_kb, p.vs.n);
       const int32_t raw2 = static_cast<int32_t>(raw_id(tt + 2));
       f32x16 sa, sb;
+      // The QK phase (MFMAs and the tile loads) runs at raised wavefront
+      // priority, so the SIMD's other wavefront fills in with its softmax.
+      __builtin_amdgcn_s_setprio(2);
       qk(k_cur, sa, sb, [&](int st) {
         // load i of the 2 * kInstPerWave loads (K, then V) follows k-step
         // i * kSteps / (2 * kInstPerWave): all of tile t+1 is in flight before
@@ -409,6 +412,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
           }
         }
       });
+      __builtin_amdgcn_s_setprio(0);
       mask_keys(j0, sa, sb);
       bf16x8 pb[4];
       weights(sa, sb, pb);
