@@ -237,11 +237,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
     ld_koff[e] = static_cast<uint32_t>((r * p.ks.n + 8 * (pc ^ swz_k<D>(r))) * 2);
     ld_voff[e] = static_cast<uint32_t>((r * p.vs.n + 8 * (pc ^ swz_v<D>(r))) * 2);
   }
-  auto tile_rsrc = [&](const uint16_t* base, int64_t j, int64_t rs) {
-    int64_t rows = p.N - j * kKBlock;
-    rows = rows < 0 ? 0 : (rows > kKBlock ? kKBlock : rows);
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + j * kKBlock * rs), static_cast<short>(0),
-                                             static_cast<int>(rows * rs * 2), kBufferFlags);
+  // Tile j of an operand starts j * tile_bytes past its head; its bound is the
+  // whole tile, the rows left at the sequence end, or nothing (j past the end).
+  const int64_t n_full = p.N / kKBlock;
+  const uint32_t k_tile = static_cast<uint32_t>(kKBlock * p.ks.n * 2);
+  const uint32_t v_tile = static_cast<uint32_t>(kKBlock * p.vs.n * 2);
+  const uint32_t k_tail = static_cast<uint32_t>((p.N - n_full * kKBlock) * p.ks.n * 2);
+  const uint32_t v_tail = static_cast<uint32_t>((p.N - n_full * kKBlock) * p.vs.n * 2);
+  auto tile_rsrc = [&](const uint16_t* base, int64_t j, uint32_t tile_bytes, uint32_t tail_bytes) {
+    const uint32_t bound = j < n_full ? tile_bytes : (j == n_full ? tail_bytes : 0u);
+    const char* ptr = reinterpret_cast<const char*>(base) +
+                      static_cast<uint64_t>(static_cast<uint32_t>(j)) * tile_bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(ptr), static_cast<short>(0),
+                                             static_cast<int>(bound), kBufferFlags);
   };
   auto issue_one = [&](__amdgpu_buffer_rsrc_t rs, uint32_t off, char* buf, int e) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + (wave_s * C::kInstPerWave + e) * 1024),
@@ -255,8 +263,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
     __builtin_amdgcn_sched_barrier(kSchedKeepLoads);
   };
   auto issue = [&](int64_t j, char* kbuf, char* vbuf) {
-    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kh, j, p.ks.n);
-    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vh, j, p.vs.n);
+    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kh, j, k_tile, k_tail);
+    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vh, j, v_tile, v_tail);
 #pragma unroll
     for (int e = 0; e < C::kInstPerWave; ++e) {
       issue_one(kr, ld_koff[e], kbuf, e);
@@ -392,8 +400,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
       const bool more = tt + 1 < cnt;
       // past the last tile the resources hold no bytes: the loads only write
       // zeros into the buffer that was just released
-      const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kh, more ? j1 : p.n_kb, p.ks.n);
-      const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vh, more ? j1 : p.n_kb, p.vs.n);
+      const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kh, more ? j1 : p.n_kb, k_tile, k_tail);
+      const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vh, more ? j1 : p.n_kb, v_tile, v_tail);
       const int32_t raw2 = static_cast<int32_t>(raw_id(tt + 2));
       f32x16 sa, sb;
       // The QK phase (MFMAs and the tile loads) runs at raised wavefront
