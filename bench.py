@@ -143,7 +143,7 @@ def load_traffic(workload: str):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, q, k, v, topk, budget_s, causal=False):
+def cpu_baseline(wl, q, k, v, topk, budget_s, causal=False, tau=None):
     """The fp64 oracle on the host cores: head 0's full prediction plus attention for as
     many of its query blocks as fit in the time budget (in block order)."""
     import oracle
@@ -161,7 +161,10 @@ def cpu_baseline(wl, q, k, v, topk, budget_s, causal=False):
         f64 = synth.bf16_bits_to_f64
         qh, kh, vh = f64(q[0, 0]), f64(k[0, 0]), f64(v[0, 0])
         t0 = time.perf_counter()
-        pr = oracle.predict_mask(qh[None, None], kh[None, None], topk, causal=causal)
+        if tau is None:
+            pr = oracle.predict_mask(qh[None, None], kh[None, None], topk, causal=causal)
+        else:
+            pr = oracle.predict_mask_cdf(qh[None, None], kh[None, None], tau, causal=causal)
         t_pred = time.perf_counter() - t0
         m = pr["mask"][0, 0]
         qb = m.shape[0]
@@ -270,6 +273,10 @@ def main():
         sp.pool_blocks(dq, 128)
         sp.pool_blocks(dk, 64)
         sp.predict_mask(qbar, kbar, N, topk, is_causal=causal)
+        sp.compact_mask(mask_t, N)
+        if wl.grid is not None:
+            perm_k = sp.token_permutation(wl.n_text, wl.grid, "cube").to(dev)
+            sp.permute_tokens(dq, perm_k, out=out)
         dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"kernels_only": True, "copy_bytes": COPY_BYTES, "workload": wl.name,
@@ -378,7 +385,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle sample")
-        result["cpu_baseline"] = cpu_baseline(wl, q, k, v, topk, args.cpu_seconds, causal)
+        result["cpu_baseline"] = cpu_baseline(wl, q, k, v, topk, args.cpu_seconds, causal, args.tau)
     print(json.dumps(result), flush=True)
 
 
