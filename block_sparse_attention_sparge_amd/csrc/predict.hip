@@ -19,7 +19,7 @@
 // integer sums are exact in any order; the cut is found by the same radix
 // select with weight histograms instead of counts.
 //
-// One workgroup (4 wavefronts) takes R query blocks of one head. Scores for
+// One workgroup (8 wavefronts) takes R <= 8 query blocks of one head. Scores for
 // all R rows live in LDS. Selection is an exact radix select on order-preserving
 // 32-bit keys (4 passes of 8 bits, LDS histograms, wavefront prefix sums), one
 // wavefront per row; the final pass emits the list in index order with ballots.
@@ -29,7 +29,7 @@
 namespace sparge {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 
 // Float -> uint32 whose unsigned order matches the float order (-0 folded to +0).
@@ -53,24 +53,27 @@ __device__ __forceinline__ uint32_t count_below(uint64_t m) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
 }
 
-// Stages the R pooled query rows of a group (zeros past the last query block)
-// and writes their fp32 scores against every key block of the head to sc.
+// Writes the fp32 scores of the R pooled query rows of a group (rows past the
+// last query block repeat it; their scores are never read) against every key
+// block of the head to sc. The query rows are wavefront-uniform, so they are
+// read through the scalar cache and feed the FMAs as scalar operands.
 template <int D, int R>
 __device__ __forceinline__ void pooled_scores(const float* __restrict__ qbar, const float* __restrict__ kbar,
                                               int64_t bh, int64_t row0, int64_t n_qb, int64_t n_kb,
-                                              float scale, float* q_lds, float* sc) {
+                                              float scale, float* sc) {
+  typedef float fv4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(4))) const fv4 cfloat4;
   const int t = threadIdx.x;
-  for (int e = t; e < R * D; e += kThreads) {
-    const int r = e / D;
-    const int64_t qi = row0 + r;
-    q_lds[e] = (qi < n_qb) ? qbar[(bh * n_qb + qi) * D + (e - r * D)] : 0.f;
+  cfloat4* qrow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t qi = (row0 + r < n_qb) ? row0 + r : n_qb - 1;
+    qrow[r] = (cfloat4*)(qbar + (bh * n_qb + qi) * D);
   }
-  __syncthreads();
-
-  // Scores: thread t takes key blocks t, t+256, ... and all R rows.
+  // thread t takes key blocks t, t+256, ... and all R rows
   const float* kb_head = kbar + bh * n_kb * D;
-  for (int64_t j = t; j < n_kb; j += kThreads) {
-    const float4* kr = reinterpret_cast<const float4*>(kb_head + j * D);
+  for (int j = t; j < n_kb; j += kThreads) {
+    const float4* kr = reinterpret_cast<const float4*>(kb_head + static_cast<int64_t>(j) * D);
     float acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = 0.f;
@@ -79,7 +82,7 @@ __device__ __forceinline__ void pooled_scores(const float* __restrict__ qbar, co
       const float4 kv = kr[d4];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const float4 qv = reinterpret_cast<const float4*>(q_lds + r * D)[d4];
+        const fv4 qv = qrow[r][d4];
         acc[r] = fmaf(qv.x, kv.x, acc[r]);
         acc[r] = fmaf(qv.y, kv.y, acc[r]);
         acc[r] = fmaf(qv.z, kv.z, acc[r]);
@@ -106,8 +109,7 @@ __global__ __launch_bounds__(kThreads) void predict_kernel(
     int64_t n_kb, int64_t n_groups, int64_t k, double topk, int causal, float scale,
     uint8_t* __restrict__ mask, int32_t* __restrict__ kv_idx, int32_t* __restrict__ kv_cnt) {
   extern __shared__ float4 smem4[];
-  float* q_lds = reinterpret_cast<float*>(smem4);          // [R][D]
-  float* sc = q_lds + R * D;                               // [R][n_kb]
+  float* sc = reinterpret_cast<float*>(smem4);             // [R][n_kb]
   uint32_t* hist = reinterpret_cast<uint32_t*>(sc + R * n_kb);   // [kWaves][256]
 
   const int64_t bh = blockIdx.x / n_groups;
@@ -115,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void predict_kernel(
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
-  pooled_scores<D, R>(qbar, kbar, bh, row0, n_qb, n_kb, scale, q_lds, sc);
+  pooled_scores<D, R>(qbar, kbar, bh, row0, n_qb, n_kb, scale, sc);
 
   // Selection: wavefront `wave` takes rows wave, wave + 4, ...; every wavefront
   // runs the same number of rounds so the block-wide barriers stay uniform.
@@ -238,17 +240,16 @@ __global__ __launch_bounds__(kThreads) void predict_cdf_kernel(
     int64_t n_kb, int64_t n_groups, double tau, int causal, float scale,
     uint8_t* __restrict__ mask, int32_t* __restrict__ kv_idx, int32_t* __restrict__ kv_cnt) {
   extern __shared__ float4 smem4[];
-  float* q_lds = reinterpret_cast<float*>(smem4);          // [R][D]
-  float* sc = q_lds + R * D;                               // [R][n_kb]
+  float* sc = reinterpret_cast<float*>(smem4);             // [R][n_kb]
   // [kWaves][256] 64-bit weight histograms, 8-byte aligned after the scores
-  uint64_t* hist = reinterpret_cast<uint64_t*>(q_lds + ((R * D + R * n_kb + 1) & ~int64_t(1)));
+  uint64_t* hist = reinterpret_cast<uint64_t*>(sc + ((R * n_kb + 1) & ~int64_t(1)));
 
   const int64_t bh = blockIdx.x / n_groups;
   const int64_t row0 = (blockIdx.x - bh * n_groups) * R;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
-  pooled_scores<D, R>(qbar, kbar, bh, row0, n_qb, n_kb, scale, q_lds, sc);
+  pooled_scores<D, R>(qbar, kbar, bh, row0, n_qb, n_kb, scale, sc);
 
   uint64_t* h = hist + wave * 256;
   constexpr int kRounds = (R + kWaves - 1) / kWaves;
@@ -352,7 +353,7 @@ hipError_t launch_predict_t(const float* qbar, const float* kbar, int64_t BH, in
                             int64_t n_kb, int64_t k, double topk, int causal, float scale,
                             uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt, hipStream_t stream) {
   const int64_t n_groups = (n_qb + R - 1) / R;
-  const size_t lds = sizeof(float) * (R * D + R * n_kb) + sizeof(uint32_t) * kWaves * 256;
+  const size_t lds = sizeof(float) * R * n_kb + sizeof(uint32_t) * kWaves * 256;
   void* args[] = {(void*)&qbar, (void*)&kbar, (void*)&N, (void*)&n_qb, (void*)&n_kb,
                   (void*)&n_groups, (void*)&k, (void*)&topk, (void*)&causal, (void*)&scale,
                   (void*)&mask, (void*)&kv_idx, (void*)&kv_cnt};
@@ -365,11 +366,11 @@ template <int D>
 hipError_t launch_predict_d(const float* qbar, const float* kbar, int64_t BH, int64_t N, int64_t n_qb,
                             int64_t n_kb, int64_t k, double topk, int causal, float scale,
                             uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt, hipStream_t stream) {
-  if (n_kb <= 1536)
+  if (n_kb <= 2304)
     return launch_predict_t<D, 8>(qbar, kbar, BH, N, n_qb, n_kb, k, topk, causal, scale, mask, kv_idx, kv_cnt, stream);
-  if (n_kb <= 3072)
+  if (n_kb <= 4608)
     return launch_predict_t<D, 4>(qbar, kbar, BH, N, n_qb, n_kb, k, topk, causal, scale, mask, kv_idx, kv_cnt, stream);
-  if (n_kb <= 6144)
+  if (n_kb <= 9216)
     return launch_predict_t<D, 2>(qbar, kbar, BH, N, n_qb, n_kb, k, topk, causal, scale, mask, kv_idx, kv_cnt, stream);
   return launch_predict_t<D, 1>(qbar, kbar, BH, N, n_qb, n_kb, k, topk, causal, scale, mask, kv_idx, kv_cnt, stream);
 }
@@ -379,7 +380,7 @@ hipError_t launch_cdf_t(const float* qbar, const float* kbar, int64_t BH, int64_
                         int64_t n_kb, double tau, int causal, float scale, uint8_t* mask,
                         int32_t* kv_idx, int32_t* kv_cnt, hipStream_t stream) {
   const int64_t n_groups = (n_qb + R - 1) / R;
-  const size_t lds = sizeof(float) * ((R * D + R * n_kb + 1) & ~int64_t(1)) + sizeof(uint64_t) * kWaves * 256;
+  const size_t lds = sizeof(float) * ((R * n_kb + 1) & ~int64_t(1)) + sizeof(uint64_t) * kWaves * 256;
   void* args[] = {(void*)&qbar, (void*)&kbar, (void*)&N, (void*)&n_qb, (void*)&n_kb,
                   (void*)&n_groups, (void*)&tau, (void*)&causal, (void*)&scale,
                   (void*)&mask, (void*)&kv_idx, (void*)&kv_cnt};
@@ -392,11 +393,11 @@ template <int D>
 hipError_t launch_cdf_d(const float* qbar, const float* kbar, int64_t BH, int64_t N, int64_t n_qb,
                         int64_t n_kb, double tau, int causal, float scale, uint8_t* mask,
                         int32_t* kv_idx, int32_t* kv_cnt, hipStream_t stream) {
-  if (n_kb <= 1536)
+  if (n_kb <= 2304)
     return launch_cdf_t<D, 8>(qbar, kbar, BH, N, n_qb, n_kb, tau, causal, scale, mask, kv_idx, kv_cnt, stream);
-  if (n_kb <= 3072)
+  if (n_kb <= 4608)
     return launch_cdf_t<D, 4>(qbar, kbar, BH, N, n_qb, n_kb, tau, causal, scale, mask, kv_idx, kv_cnt, stream);
-  if (n_kb <= 6144)
+  if (n_kb <= 9216)
     return launch_cdf_t<D, 2>(qbar, kbar, BH, N, n_qb, n_kb, tau, causal, scale, mask, kv_idx, kv_cnt, stream);
   return launch_cdf_t<D, 1>(qbar, kbar, BH, N, n_qb, n_kb, tau, causal, scale, mask, kv_idx, kv_cnt, stream);
 }

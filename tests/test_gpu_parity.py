@@ -473,6 +473,32 @@ def test_attn_cdf(gpu_lib, B, H, N, D, causal):
     assert rep["failures"] == 0, rep
 
 
+# Rows of 2304 key blocks are the longest that eight share a workgroup's LDS;
+# one more key block halves the rows per workgroup.
+@pytest.mark.parametrize("N", [2304 * 64, 2304 * 64 + 1])
+@pytest.mark.parametrize("mode", ["topk", "cdf"])
+def test_predict_workgroup_sizes(gpu_lib, N, mode):
+    D = 64
+    wl = synth.custom(1, 1, N, D, config_id=301)
+    q, k = synth.make_tensor(wl, "q"), synth.make_tensor(wl, "k")
+    print(f"N={N} mode={mode}", flush=True)
+    qbar, kbar = sp.pool_blocks(to_dev(q), 128), sp.pool_blocks(to_dev(k), 64)
+    if mode == "topk":
+        mask, idx, cnt = sp.predict_mask(qbar, kbar, N, 0.2)
+        m = mask.cpu().numpy()
+        rep = oracle_mask_parity(lambda b, h: F64(q[b, h]), lambda b, h: F64(k[b, h]), 0.2, m)
+    else:
+        mask, idx, cnt = sp.predict_mask_cdf(qbar, kbar, N, 0.5, scale=8.0)
+        m = mask.cpu().numpy()
+        rep = _cdf_parity(q, k, 0.5, m, 8.0)
+    print(rep, flush=True)
+    assert rep["failures"] == 0, rep
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    assert (cnt == m.sum(-1)).all()
+    for i in range(m.shape[2]):
+        assert idx[0, 0, i, : cnt[0, 0, i]].tolist() == np.flatnonzero(m[0, 0, i]).tolist()
+
+
 @pytest.mark.parametrize("cfg,tau", [(1, 0.9), (2, 0.8)], ids=["cfg1-tau0.9", "cfg2-tau0.8"])
 def test_cdf_workload_parity(gpu_lib, cfg, tau):
     """CDF selection at a workload's full size: every mask row, sampled output rows."""
