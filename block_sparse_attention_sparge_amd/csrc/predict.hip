@@ -70,7 +70,7 @@ __device__ __forceinline__ void pooled_scores(const float* __restrict__ qbar, co
     const int64_t qi = (row0 + r < n_qb) ? row0 + r : n_qb - 1;
     qrow[r] = (cfloat4*)(qbar + (bh * n_qb + qi) * D);
   }
-  // thread t takes key blocks t, t+256, ... and all R rows
+  // thread t takes key blocks t, t + kThreads, ... and all R rows
   const float* kb_head = kbar + bh * n_kb * D;
   for (int j = t; j < n_kb; j += kThreads) {
     const float4* kr = reinterpret_cast<const float4*>(kb_head + static_cast<int64_t>(j) * D);
