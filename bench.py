@@ -197,6 +197,27 @@ def cpu_baseline(wl, q, k, v, topk, budget_s, causal=False, tau=None):
             ctx.__exit__(None, None, None)
 
 
+def device_info(torch) -> dict:
+    """CU count and clocks the runtime reports for device 0 (rocminfo when present)."""
+    props = torch.cuda.get_device_properties(0)
+    info = {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "max_clock_mhz": None}
+    try:
+        import subprocess
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=30).stdout
+        for agent in txt.split("Agent ")[1:]:
+            if "gfx9" in agent and "Compute Unit:" in agent:
+                for line in agent.splitlines():
+                    if "Max Clock Freq. (MHz):" in line:
+                        info["max_clock_mhz"] = int(line.split(":")[1].split()[0])
+                    if "Compute Unit:" in line:
+                        info["rocminfo_compute_units"] = int(line.split(":")[1].split()[0])
+                break
+    except (OSError, ValueError, subprocess.SubprocessError):
+        pass
+    return info
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -378,6 +399,7 @@ def main():
                     "gflops_fp32": pred_flops / (np.mean(pred) * 1e-3) / 1e9,
                     "gbs": pred_bytes / (np.mean(pred) * 1e-3) / 1e9},
         "layout": layout_info,
+        "device": device_info(torch),
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": None if (causal or cdf or layout != "raster") else load_traffic(f"{wl.name}_topk{topk}"),

@@ -22,9 +22,10 @@ import os
 import torch
 
 __all__ = [
-    "Q_BLOCK", "K_BLOCK", "SpargeError", "SpargeArgumentError", "load_library", "library_path", "topk_count",
-    "workspace_bytes", "pool_blocks", "predict_mask", "compact_mask", "attn_from_list",
-    "block_sparse_attn", "attn_topk", "mask_shape",
+    "Q_BLOCK", "K_BLOCK", "LAYOUTS", "SpargeError", "SpargeArgumentError", "load_library", "library_path",
+    "topk_count", "workspace_bytes", "pool_blocks", "predict_mask", "predict_mask_cdf", "compact_mask",
+    "attn_from_list", "block_sparse_attn", "attn_topk", "attn_cdf", "mask_shape", "token_permutation",
+    "permute_tokens",
 ]
 
 Q_BLOCK = 128
@@ -135,6 +136,33 @@ def _operand(t: torch.Tensor, name: str) -> torch.Tensor:
     return t if _fits(t) else t.contiguous()
 
 
+def _output(out, like: torch.Tensor, name: str = "out") -> torch.Tensor:
+    """A new output shaped like `like`, or a checked caller-supplied one (written in place)."""
+    if out is None:
+        return torch.empty_like(like)
+    if (not isinstance(out, torch.Tensor) or out.dtype != torch.bfloat16 or out.device != like.device
+            or tuple(out.shape) != tuple(like.shape)):
+        raise ValueError(f"{name} must be a bfloat16 tensor of shape {tuple(like.shape)} on {like.device}")
+    if not _fits(out):
+        raise ValueError(f"{name} must be unit-stride in its last dimension, with the other strides "
+                         "multiples of 8 elements and a 16-byte aligned start")
+    return out
+
+
+def _on_device(t: torch.Tensor, dev: torch.device, name: str) -> None:
+    if not isinstance(t, torch.Tensor) or t.device != dev:
+        raise ValueError(f"{name} must be a tensor on {dev}")
+
+
+def _pooled(qbar, kbar):
+    for t, name in ((qbar, "qbar"), (kbar, "kbar")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_cuda or t.dim() != 4:
+            raise ValueError(f"{name} must be a (B, H, blocks, D) float32 tensor on a GPU device")
+    if qbar.device != kbar.device:
+        raise ValueError("qbar and kbar must be on the same device")
+    return qbar.contiguous(), kbar.contiguous()
+
+
 def _qkv(q, k, v):
     q, k, v = _operand(q, "q"), _operand(k, "k"), _operand(v, "v")
     if not (q.shape == k.shape == v.shape):
@@ -177,6 +205,7 @@ def _workspace(t, B, H, N, D, topk, workspace):
     need = workspace_bytes(B, H, N, D, topk)
     if workspace is None:
         return torch.empty(max(need, 16), dtype=torch.uint8, device=t.device)
+    _on_device(workspace, t.device, "workspace")
     if workspace.numel() * workspace.element_size() < need or not workspace.is_contiguous():
         raise ValueError(f"workspace must be a contiguous buffer of at least {need} bytes")
     return workspace
@@ -199,9 +228,7 @@ def predict_mask(qbar: torch.Tensor, kbar: torch.Tensor, N: int, topk: float, sc
     With is_causal=True, query block i ranks only the key blocks holding a key
     one of its rows may see and keeps the top-k share of those (kv_cnt per row).
     """
-    if qbar.dtype != torch.float32 or kbar.dtype != torch.float32:
-        raise ValueError("qbar and kbar must be float32")
-    qbar, kbar = qbar.contiguous(), kbar.contiguous()
+    qbar, kbar = _pooled(qbar, kbar)
     B, H, n_qb, D = qbar.shape
     n_kb = kbar.shape[2]
     if (n_qb, n_kb) != mask_shape(B, H, N)[2:] or kbar.shape[:2] != (B, H) or kbar.shape[3] != D:
@@ -218,6 +245,8 @@ def predict_mask(qbar: torch.Tensor, kbar: torch.Tensor, N: int, topk: float, sc
 
 
 def _mask_u8(mask_id, B, H, N, dev):
+    if not isinstance(mask_id, torch.Tensor) or not mask_id.is_cuda:
+        raise ValueError("mask_id must be a tensor on a GPU device")
     if mask_id.shape != mask_shape(B, H, N):
         raise ValueError(f"mask_id must have shape {mask_shape(B, H, N)}, got {tuple(mask_id.shape)}")
     if mask_id.device != dev:
@@ -242,11 +271,13 @@ def attn_from_list(q, k, v, kv_idx=None, kv_cnt=None, scale=None, out=None, is_c
     """Attention over precomputed kept-block lists (kv_idx None: dense)."""
     q, k, v = _qkv(q, k, v)
     B, H, N, D = q.shape
-    out = torch.empty_like(q) if out is None else out
+    out = _output(out, q)
     ld = 0
     if kv_idx is not None:
         if kv_idx.dtype != torch.int32 or kv_cnt is None or kv_cnt.dtype != torch.int32:
             raise ValueError("kv_idx and kv_cnt must be int32")
+        _on_device(kv_idx, q.device, "kv_idx")
+        _on_device(kv_cnt, q.device, "kv_cnt")
         kv_idx, kv_cnt = kv_idx.contiguous(), kv_cnt.contiguous()
         if kv_idx.shape[:3] != mask_shape(B, H, N)[:3] or kv_cnt.shape != kv_idx.shape[:3]:
             raise ValueError("kv_idx / kv_cnt shapes do not match q")
@@ -265,7 +296,7 @@ def block_sparse_attn(q, k, v, mask_id=None, scale=None, out=None, workspace=Non
     """
     q, k, v = _qkv(q, k, v)
     B, H, N, D = q.shape
-    out = torch.empty_like(q) if out is None else out
+    out = _output(out, q)
     ws = None
     nbytes = 0
     if mask_id is not None:
@@ -289,7 +320,7 @@ def attn_topk(q, k, v, topk=0.5, is_causal=False, scale=None, return_mask=False,
     """
     q, k, v = _qkv(q, k, v)
     B, H, N, D = q.shape
-    out = torch.empty_like(q) if out is None else out
+    out = _output(out, q)
     mask = torch.empty(mask_shape(B, H, N), dtype=torch.uint8, device=q.device) if return_mask else None
     ws = _workspace(q, B, H, N, D, topk, workspace)
     _check("sparge_attn_topk", load_library().sparge_attn_topk(
@@ -324,7 +355,7 @@ def permute_tokens(x: torch.Tensor, perm: torch.Tensor, inverse: bool = False, o
     if perm.dtype != torch.int32 or perm.device != x.device or perm.numel() != N:
         raise ValueError("perm must be an int32 tensor of N entries on x's device")
     perm = perm.contiguous()
-    out = torch.empty_like(x) if out is None else out
+    out = _output(out, x)
     _check("sparge_permute_tokens", load_library().sparge_permute_tokens(
         _ptr(x), _ptr(perm), _ptr(out), B, H, N, D, _strides(x), _strides(out), int(bool(inverse)),
         _stream(x)))
@@ -336,9 +367,7 @@ def predict_mask_cdf(qbar: torch.Tensor, kbar: torch.Tensor, N: int, tau: float,
     """CDF-threshold block selection from pooled means: per query block, key blocks in
     decreasing probability until their sum reaches tau. Returns (mask_id or None,
     kv_idx (B, H, Qb, Kb), kv_cnt)."""
-    if qbar.dtype != torch.float32 or kbar.dtype != torch.float32:
-        raise ValueError("qbar and kbar must be float32")
-    qbar, kbar = qbar.contiguous(), kbar.contiguous()
+    qbar, kbar = _pooled(qbar, kbar)
     B, H, n_qb, D = qbar.shape
     n_kb = kbar.shape[2]
     if (n_qb, n_kb) != mask_shape(B, H, N)[2:] or kbar.shape[:2] != (B, H) or kbar.shape[3] != D:
@@ -360,7 +389,7 @@ def attn_cdf(q, k, v, tau=0.9, is_causal=False, scale=None, return_mask=False, o
     """
     q, k, v = _qkv(q, k, v)
     B, H, N, D = q.shape
-    out = torch.empty_like(q) if out is None else out
+    out = _output(out, q)
     mask = torch.empty(mask_shape(B, H, N), dtype=torch.uint8, device=q.device) if return_mask else None
     ws = _workspace(q, B, H, N, D, 1.0, workspace)
     _check("sparge_attn_cdf", load_library().sparge_attn_cdf(

@@ -518,3 +518,56 @@ def test_cdf_workload_parity(gpu_lib, cfg, tau):
         got = synth.bf16_bits_to_f64(outs[b, h, torch.from_numpy(rows).cuda()].cpu().numpy().view(np.uint16))
         ref = oracle.masked_attention_rows(F64(q[b, h]), F64(k[b, h]), F64(v[b, h]), m[b, h], rows)
         print(assert_close(got, ref, f"cdf cfg{cfg} head {(b, h)}"), flush=True)
+
+
+# ------------------------------------------------------------ binding argument checks
+
+def test_binding_rejects_misplaced_buffers(gpu_lib):
+    """Outputs, lists, masks and workspaces that do not match q are refused before any launch."""
+    B, H, N, D = 1, 2, 300, 64
+    q, k, v = _dev(*rand_qkv(B, H, N, D, seed=5))
+    qbar, kbar = sp.pool_blocks(q, 128), sp.pool_blocks(k, 64)
+    mask, idx, cnt = sp.predict_mask(qbar, kbar, N, 0.5)
+    bad_outs = [torch.empty(B, H, N - 1, D, dtype=torch.bfloat16, device="cuda"),   # wrong shape
+                torch.empty(B, H, N, D, dtype=torch.float32, device="cuda"),        # wrong dtype
+                torch.empty(B, H, N, D, dtype=torch.bfloat16),                      # host memory
+                torch.empty(B, H, D, N, dtype=torch.bfloat16, device="cuda").transpose(2, 3)]  # D strided
+    for bad in bad_outs:
+        for call in (lambda o: sp.attn_topk(q, k, v, topk=0.5, out=o),
+                     lambda o: sp.block_sparse_attn(q, k, v, mask_id=mask, out=o),
+                     lambda o: sp.attn_from_list(q, k, v, idx, cnt, out=o),
+                     lambda o: sp.attn_cdf(q, k, v, tau=0.5, out=o)):
+            with pytest.raises(ValueError):
+                call(bad)
+    with pytest.raises(ValueError):
+        sp.attn_from_list(q, k, v, idx.cpu(), cnt)
+    with pytest.raises(ValueError):
+        sp.attn_from_list(q, k, v, idx, cnt.cpu())
+    with pytest.raises(ValueError):
+        sp.block_sparse_attn(q, k, v, mask_id=mask.cpu())
+    with pytest.raises(ValueError):
+        sp.compact_mask(mask.cpu(), N)
+    with pytest.raises(ValueError):
+        sp.predict_mask(qbar.cpu(), kbar, N, 0.5)
+    with pytest.raises(ValueError):
+        sp.predict_mask_cdf(qbar, kbar.cpu(), N, 0.5)
+    ws = torch.empty(sp.workspace_bytes(B, H, N, D, 0.5), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        sp.attn_topk(q, k, v, topk=0.5, workspace=ws)
+    with pytest.raises(ValueError):
+        sp.permute_tokens(q, torch.arange(N, dtype=torch.int32), out=None)   # host permutation
+    torch.cuda.synchronize()
+
+
+def test_strided_output(gpu_lib):
+    """A caller's output view with padded rows receives the same bytes as a fresh tensor."""
+    B, H, N, D = 2, 2, 700, 64
+    q, k, v = _dev(*rand_qkv(B, H, N, D, seed=6))
+    ref = sp.attn_topk(q, k, v, topk=0.4)
+    big = torch.full((B, N, H, 2 * D), -7.0, dtype=torch.bfloat16, device="cuda")
+    view = big[..., :D].transpose(1, 2)          # (B, H, N, D), token stride H * 2D
+    got = sp.attn_topk(q, k, v, topk=0.4, out=view)
+    torch.cuda.synchronize()
+    assert got.data_ptr() == view.data_ptr()
+    assert torch.equal(view.contiguous().view(torch.int16), ref.view(torch.int16))
+    assert bool((big[..., D:] == -7.0).all())   # padding untouched
