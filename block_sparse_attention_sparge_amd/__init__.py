@@ -132,8 +132,9 @@ def _operand(t: torch.Tensor, name: str) -> torch.Tensor:
         raise ValueError(f"{name} must be (B, H, N, D)")
     if t.shape[-1] not in (64, 128):
         raise ValueError(f"{name}: head dimension must be 64 or 128 (got {t.shape[-1]})")
-    # the kernels read 16-byte rows; other layouts are copied once into one that fits
-    return t if _fits(t) else t.contiguous()
+    # the kernels read 16-byte rows, and K/V tiles as whole non-overlapping rows;
+    # other layouts (e.g. a token axis expanded with stride 0) are copied once
+    return t if (_fits(t) and t.stride(2) >= t.shape[-1]) else t.contiguous()
 
 
 def _output(out, like: torch.Tensor, name: str = "out") -> torch.Tensor:

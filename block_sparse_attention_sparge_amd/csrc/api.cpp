@@ -121,6 +121,9 @@ int check_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t
   // the attention kernel addresses the rows of one 64-key tile with 32-bit byte offsets
   for (const int64_t* s : {qs, ks, vs})
     if (s[2] > kMaxRowStride) return SPARGE_ERR_STRIDE;
+  // K and V tiles are read as 64 whole rows bounded by 64 token strides, so
+  // their rows must not overlap (a token stride of at least D)
+  if (ks[2] < D || vs[2] < D) return SPARGE_ERR_STRIDE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SPARGE_ERR_STRIDE;
   if (!non_overlapping(B, H, N, D, os)) return SPARGE_ERR_STRIDE;
   const Range ro = range_bf16(out, B, H, N, D, os);

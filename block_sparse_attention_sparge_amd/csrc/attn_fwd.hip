@@ -307,10 +307,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   };
 
   // Probabilities of a tile as bf16 PV operands, against reference mref (log2
-  // units); returns this lane's sum of the rounded weights.
+  // units); returns this lane's sum of the rounded weights (two independent
+  // dot2 chains).
   auto probs = [&](const f32x16& s0, const f32x16& s1, float mref, bf16x8 (&pb)[4]) -> float {
     const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-    float lt = 0.f;
+    float la = 0.f, lb = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
       const f32x2 e0 = {__builtin_amdgcn_exp2f(fmaf(s0[i], p.c, -mref)),
@@ -323,25 +324,28 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
       pb[i >> 3][(i & 7) + 1] = b0[1];
       pb[2 + (i >> 3)][i & 7] = b1[0];
       pb[2 + (i >> 3)][(i & 7) + 1] = b1[1];
-      lt = __builtin_amdgcn_fdot2_f32_bf16(b0, ones, lt, false);
-      lt = __builtin_amdgcn_fdot2_f32_bf16(b1, ones, lt, false);
+      la = __builtin_amdgcn_fdot2_f32_bf16(b0, ones, la, false);
+      lb = __builtin_amdgcn_fdot2_f32_bf16(b1, ones, lb, false);
     }
-    return lt;
+    return la + lb;
   };
 
   // Softmax weights of a tile. The running max m only serves as a reference
   // that keeps the weights in range, so it is not recomputed per tile: the
   // weights are taken against the current m, and only when a lane's weights
-  // sum past 2^kSumLog2 (a score far above m; or m still unset) is the tile's
-  // exact row max taken, m raised to it, O and l rescaled, and the weights
-  // recomputed. Weights up to 2^kSumLog2 are as exact in bf16 and fp32 as
-  // weights below 1, and the accumulators have ample range for them.
+  // sum past 2^kSumLog2 (a score far above m), or some lane of the wavefront
+  // has no reference yet, is the tile's exact row max taken, m raised to it, O
+  // and l rescaled, and the weights recomputed. Weights up to 2^kSumLog2 are
+  // as exact in bf16 and fp32 as weights below 1, and the accumulators have
+  // ample range for them. (A row without a reference takes the exact path
+  // whatever its weights: against the placeholder reference 0 they may all
+  // have underflowed to zero.)
   auto weights = [&](const f32x16& s0, const f32x16& s1, bf16x8 (&pb)[4]) {
     // m stays -inf only while every key seen so far was masked (invalid ids);
     // a reference of 0 then gives zero weights instead of NaN.
     float mref = (m == -INFINITY) ? 0.f : m;
     float lt = probs(s0, s1, mref, pb);
-    if (__builtin_amdgcn_ballot_w64(!(lt <= kSumLimit) || (m == -INFINITY && lt > 0.f))) {
+    if (__builtin_amdgcn_ballot_w64(m == -INFINITY || !(lt <= kSumLimit))) {
       float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));

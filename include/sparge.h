@@ -28,7 +28,8 @@
  *    top-k API is a drop-in for it). Their element strides for the B, H and N
  *    axes are passed as int64_t[3]; the D axis must be contiguous. Every
  *    stride must be a non-negative multiple of 8 elements (the token stride of
- *    Q, K and V at most 2^24 elements) and every base
+ *    Q, K and V at most 2^24 elements, and that of K and V at least D, so
+ *    that their rows do not overlap) and every base
  *    address 16-byte aligned, so that a row of 8 bf16 is one aligned load.
  *  - D (head dimension) must be 64 or 128. N >= 1, B >= 1, H >= 1.
  *  - N_QB = ceil(N/128) query blocks and N_KB = ceil(N/64) key blocks.

@@ -103,6 +103,8 @@ def test_attention_argument_errors(lib, fn):
     assert attn_call(lib, fn, qs=S(2 * 256 * 64, 256 * 64, 60), mask=mask) == STRIDE   # not a multiple of 8
     assert attn_call(lib, fn, ks=S(-8, 256 * 64, 64), mask=mask) == STRIDE
     assert attn_call(lib, fn, q=A + 8, mask=mask) == STRIDE                          # misaligned
+    assert attn_call(lib, fn, ks=S(256 * 64, 0, 0), mask=mask) == STRIDE              # K expanded along N
+    assert attn_call(lib, fn, vs=S(2 * 256 * 32, 256 * 32, 32), mask=mask) == STRIDE  # V rows overlap
     assert attn_call(lib, fn, os_=S(2 * 256 * 64, 256 * 64, 32), mask=mask) == STRIDE  # rows overlap
     assert attn_call(lib, fn, out=A + 1024, mask=mask) == ALIAS                      # out inside q
     assert attn_call(lib, fn, out=C - 1024, mask=mask) == ALIAS                      # out runs into v

@@ -177,6 +177,28 @@ def test_softmax_reference_raised(gpu_lib, D, pattern):
     print(assert_close(to_host_f64(out), ref, f"{pattern} D={D}"))
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_softmax_far_below_zero(gpu_lib, D, causal):
+    """Every logit of every row pushed far below zero by one common offset
+    (q = x - 40 e0, k = y + 40 e0): the softmax must not depend on that shift,
+    although exp2 of the raw scores underflows to zero."""
+    B, H, N = 1, 2, 700
+    q, k, v = rand_qkv(B, H, N, D, seed=43 + D)
+    qf, kf = F64(q), F64(k)
+    qf[..., 0] -= 40.0
+    kf[..., 0] += 40.0
+    qb = synth.f32_to_bf16_bits(qf.astype(np.float32))
+    kb = synth.f32_to_bf16_bits(kf.astype(np.float32))
+    m = _random_mask(B, H, N, 0.5, seed=9, empty_rows=False)
+    m[..., 0] = 1
+    out = sp.block_sparse_attn(*_dev(qb, kb, v), mask_id=torch.from_numpy(m).cuda(), is_causal=causal)
+    ref = oracle.masked_attention(F64(qb), F64(kb), F64(v), m, causal=causal)
+    lg = (F64(qb)[0, 0, :8] @ F64(kb)[0, 0].T) / math.sqrt(D) * math.log2(math.e)
+    assert lg.max() < -150      # exp2 of any raw logit is below the smallest fp32 normal
+    print(assert_close(to_host_f64(out), ref, f"far below zero D={D} causal={causal}"))
+
+
 def test_deterministic(gpu_lib):
     wl = synth.WORKLOADS[0]
     q, k, v = synth.make_qkv(wl)
