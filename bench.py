@@ -11,7 +11,9 @@ stderr. Alongside the step it reports:
     as effective and dense-equivalent TFLOP/s against the bf16 MFMA peak;
   - pooling (GB/s) and prediction (GFLOP/s, GB/s) kernels;
   - block_sparse_attn with the predicted mask as a user mask (compaction + attention);
-  - the fp64 CPU oracle timed on the host cores on a bounded sample.
+  - the fp64 CPU oracle timed on the host cores on a bounded sample, and (in the
+    same CPU leg) every head's mask checked against the oracle's, with the count
+    of rows whose pooled-logit gap at the top-k cut is under 1e-5.
 """
 from __future__ import annotations
 
@@ -195,6 +197,36 @@ def cpu_baseline(wl, q, k, v, topk, budget_s, causal=False, tau=None):
     finally:
         if ctx:
             ctx.__exit__(None, None, None)
+
+
+def mask_parity_all_heads(q, k, m, topk, causal=False, tau=None):
+    """Every head's device mask against the oracle's prediction: rows compared, rows
+    whose pooled-logit gap at the cut is under 1e-5 (near ties), how many of those
+    differ, and failures (rows that differ outside that band). Part of the CPU leg."""
+    import oracle
+    import synth
+    f64 = synth.bf16_bits_to_f64
+    B, H = m.shape[:2]
+    tot = {"heads": B * H, "rows": 0, "near_tie_rows": 0, "differing": 0, "failures": 0}
+    t0 = time.perf_counter()
+    for b in range(B):
+        for h in range(H):
+            qh, kh = f64(q[b, h])[None, None], f64(k[b, h])[None, None]
+            if tau is None:
+                pr = oracle.predict_mask(qh, kh, topk, causal=causal)
+                rep = oracle.mask_parity(pr["logits"], pr["mask"], m[b, h][None, None], pr["k"],
+                                         probs=pr["probs"], cand=pr["cand"])
+                tot["near_tie_rows"] += rep["candidates"]
+            else:
+                pr = oracle.predict_mask_cdf(qh, kh, tau, causal=causal)
+                rep = oracle.mask_parity_cdf(pr["logits"], pr["probs"], pr["mask"], m[b, h][None, None],
+                                             tau, cand=pr["cand"])
+                tot["near_tie_rows"] += rep["excused"]
+            tot["rows"] += rep["rows"]
+            tot["differing"] += rep["differing"]
+            tot["failures"] += rep["failures"]
+    tot["seconds"] = time.perf_counter() - t0
+    return tot
 
 
 def device_info(torch) -> dict:
@@ -408,6 +440,9 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle sample")
         result["cpu_baseline"] = cpu_baseline(wl, q, k, v, topk, args.cpu_seconds, causal, args.tau)
+        if layout == "raster":
+            log("checking every head's mask against the oracle")
+            result["mask_parity"] = mask_parity_all_heads(q, k, m, topk, causal, args.tau)
     print(json.dumps(result), flush=True)
 
 

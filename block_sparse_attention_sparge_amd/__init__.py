@@ -25,7 +25,7 @@ __all__ = [
     "Q_BLOCK", "K_BLOCK", "LAYOUTS", "SpargeError", "SpargeArgumentError", "load_library", "library_path",
     "topk_count", "workspace_bytes", "pool_blocks", "predict_mask", "predict_mask_cdf", "compact_mask",
     "attn_from_list", "block_sparse_attn", "attn_topk", "attn_cdf", "mask_shape", "token_permutation",
-    "permute_tokens",
+    "permute_tokens", "check_mask",
 ]
 
 Q_BLOCK = 128
@@ -38,7 +38,7 @@ _lib = None
 _STATUS = {
     0: "SPARGE_OK", -1: "SPARGE_ERR_NULL", -2: "SPARGE_ERR_SHAPE", -3: "SPARGE_ERR_TOPK",
     -4: "SPARGE_ERR_STRIDE", -5: "SPARGE_ERR_ALIAS", -6: "SPARGE_ERR_WORKSPACE",
-    -7: "SPARGE_ERR_ARG", -8: "SPARGE_ERR_LAUNCH",
+    -7: "SPARGE_ERR_ARG", -8: "SPARGE_ERR_LAUNCH", -9: "SPARGE_ERR_MASK_VALUE",
 }
 
 
@@ -51,7 +51,8 @@ class SpargeError(RuntimeError):
 
 
 class SpargeArgumentError(SpargeError, ValueError):
-    """libsparge rejected an argument (status -1 .. -7); nothing was launched."""
+    """libsparge rejected an argument (status -1 .. -7, or -9 for a mask value other
+    than 0/1 found by a checking call); nothing was computed."""
 
 
 def library_path() -> str:
@@ -88,6 +89,9 @@ def load_library() -> ctypes.CDLL:
         "sparge_attn_cdf": (ci, [vp, vp, vp, f64, vp, i64, i64, i64, i64, s3, s3, s3, s3, f32,
                                  ci, vp, vp, sz, vp]),
         "sparge_permute_tokens": (ci, [vp, vp, vp, i64, i64, i64, i64, s3, s3, ci, vp]),
+        "sparge_check_mask": (ci, [vp, i64, i64, i64, vp, sz, vp]),
+        "block_sparse_attn_checked": (ci, [vp, vp, vp, vp, vp, i64, i64, i64, i64, s3, s3, s3, s3, f32,
+                                           ci, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -290,10 +294,14 @@ def attn_from_list(q, k, v, kv_idx=None, kv_cnt=None, scale=None, out=None, is_c
     return out
 
 
-def block_sparse_attn(q, k, v, mask_id=None, scale=None, out=None, workspace=None, is_causal=False):
+def block_sparse_attn(q, k, v, mask_id=None, scale=None, out=None, workspace=None, is_causal=False,
+                      validate=False):
     """Attention restricted to the 128x64 tiles a 0/1 mask_id selects (None: dense).
 
-    With is_causal=True each query row also ignores the keys after it.
+    With is_causal=True each query row also ignores the keys after it. With
+    validate=True the mask (uint8 or bool) is first checked on the device and a
+    value other than 0/1 raises SpargeArgumentError (SPARGE_ERR_MASK_VALUE); that
+    check synchronises the stream. Without it any nonzero entry counts as 1.
     """
     q, k, v = _qkv(q, k, v)
     B, H, N, D = q.shape
@@ -301,14 +309,31 @@ def block_sparse_attn(q, k, v, mask_id=None, scale=None, out=None, workspace=Non
     ws = None
     nbytes = 0
     if mask_id is not None:
+        if validate and isinstance(mask_id, torch.Tensor) and mask_id.dtype not in (torch.uint8, torch.bool):
+            raise ValueError("validate=True takes a uint8 or bool mask_id")
         mask_id = _mask_u8(mask_id, B, H, N, q.device)
         ws = _workspace(q, B, H, N, D, None, workspace)
         nbytes = ws.numel() * ws.element_size()
-    _check("block_sparse_attn", load_library().block_sparse_attn(
+    name = "block_sparse_attn_checked" if validate else "block_sparse_attn"
+    _check(name, getattr(load_library(), name)(
         _ptr(q), _ptr(k), _ptr(v), _ptr(mask_id), _ptr(out), B, H, N, D, _strides(q), _strides(k),
         _strides(v), _strides(out), _scale(scale, D), int(bool(is_causal)), _ptr(ws), nbytes,
         _stream(q)))
     return out
+
+
+def check_mask(mask_id: torch.Tensor, N: int, workspace=None) -> None:
+    """Raise SpargeArgumentError (SPARGE_ERR_MASK_VALUE) if a uint8 mask_id holds a value
+    other than 0 or 1; checked on the device, synchronising the stream."""
+    if not isinstance(mask_id, torch.Tensor) or mask_id.dtype != torch.uint8 or not mask_id.is_cuda:
+        raise ValueError("mask_id must be a uint8 tensor on a GPU device")
+    B, H = mask_id.shape[:2]
+    if mask_id.shape != mask_shape(B, H, N):
+        raise ValueError(f"mask_id must have shape {mask_shape(B, H, N)}, got {tuple(mask_id.shape)}")
+    mask_id = mask_id.contiguous()
+    ws = _workspace(mask_id, B, H, N, 64, None, workspace)
+    _check("sparge_check_mask", load_library().sparge_check_mask(
+        _ptr(mask_id), B, H, N, _ptr(ws), ws.numel() * ws.element_size(), _stream(mask_id)))
 
 
 def attn_topk(q, k, v, topk=0.5, is_causal=False, scale=None, return_mask=False, out=None,

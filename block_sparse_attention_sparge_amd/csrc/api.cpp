@@ -170,6 +170,7 @@ const char* sparge_status_string(int status) {
     case SPARGE_ERR_WORKSPACE: return "workspace missing or too small";
     case SPARGE_ERR_ARG: return "invalid argument";
     case SPARGE_ERR_LAUNCH: return "kernel launch failed";
+    case SPARGE_ERR_MASK_VALUE: return "mask_id holds a value other than 0 or 1";
     default: return "unknown status";
   }
 }
@@ -300,6 +301,58 @@ int block_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   a.kv_cnt = cnt;
   a.ld_idx = n_kblocks(N);
   return status_of(sparge::launch_attention(a, st));
+}
+
+int sparge_check_mask(const uint8_t* mask_id, int64_t B, int64_t H, int64_t N, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (!mask_id) return SPARGE_ERR_NULL;
+  if (int rc = check_shape(B, H, N, 64)) return rc;
+  const size_t n = static_cast<size_t>(B * H * n_qblocks(N) * n_kblocks(N));
+  // one flag per workgroup of 256 threads, each scanning >= 256 bytes
+  const int n_wg = static_cast<int>(std::min<size_t>(sparge::kCheckMaskWorkgroups, (n + 255) / 256));
+  const size_t need = static_cast<size_t>(n_wg) * sizeof(int32_t);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return SPARGE_ERR_WORKSPACE;
+  if (overlap(range_bytes(workspace, need), range_bytes(mask_id, n))) return SPARGE_ERR_ALIAS;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* bad = static_cast<int32_t*>(workspace);
+  if (int rc = status_of(sparge::launch_check_mask(mask_id, static_cast<int64_t>(n), bad, n_wg, st)))
+    return rc;
+  std::vector<int32_t> host(static_cast<size_t>(n_wg));
+  if (hipMemcpyAsync(host.data(), bad, need, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return SPARGE_ERR_LAUNCH;
+  for (int32_t f : host)
+    if (f) return SPARGE_ERR_MASK_VALUE;
+  return SPARGE_OK;
+}
+
+int block_sparse_attn_checked(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const uint8_t* mask_id, uint16_t* out, int64_t B, int64_t H, int64_t N,
+                              int64_t D, const int64_t q_strides[3], const int64_t k_strides[3],
+                              const int64_t v_strides[3], const int64_t o_strides[3], float scale,
+                              int is_causal, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int rc = check_attn(q, k, v, out, B, H, N, D, q_strides, k_strides, v_strides, o_strides)) return rc;
+  if (is_causal != 0 && is_causal != 1) return SPARGE_ERR_ARG;
+  if (mask_id) {
+    const MaskWs w = mask_layout(B, H, N);
+    if (!workspace || workspace_bytes < w.total || !aligned16(workspace)) return SPARGE_ERR_WORKSPACE;
+    const size_t rows = static_cast<size_t>(B * H * n_qblocks(N));
+    const Range rw = range_bytes(workspace, w.total);
+    const Range rm = range_bytes(mask_id, rows * n_kblocks(N));
+    const Range ro = range_bf16(out, B, H, N, D, o_strides);
+    // every check block_sparse_attn makes, before anything is launched
+    if (overlap(ro, rm) || overlap(rw, rm) || overlap(rw, ro) ||
+        overlap(rw, range_bf16(q, B, H, N, D, q_strides)) ||
+        overlap(rw, range_bf16(k, B, H, N, D, k_strides)) ||
+        overlap(rw, range_bf16(v, B, H, N, D, v_strides)))
+      return SPARGE_ERR_ALIAS;
+    // the lists region of the workspace (rows * N_KB int32: four bytes per mask
+    // byte, so never smaller than the check's flags) holds them until compaction
+    // reuses it
+    if (int rc = sparge_check_mask(mask_id, B, H, N, workspace, workspace_bytes, stream)) return rc;
+  }
+  return block_sparse_attn(q, k, v, mask_id, out, B, H, N, D, q_strides, k_strides, v_strides, o_strides,
+                           scale, is_causal, workspace, workspace_bytes, stream);
 }
 
 int sparge_attn_topk(const uint16_t* q, const uint16_t* k, const uint16_t* v, double topk,

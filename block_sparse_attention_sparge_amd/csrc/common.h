@@ -37,6 +37,10 @@ hipError_t launch_predict_cdf(const float* qbar, const float* kbar, int64_t BH, 
 hipError_t launch_compact(const uint8_t* mask, int64_t rows, int64_t n_kb, int32_t* kv_idx,
                           int32_t* kv_cnt, hipStream_t stream);
 
+// bad[w] (w < n_wg) = 1 if workgroup w saw a mask byte other than 0 or 1, else 0.
+constexpr int kCheckMaskWorkgroups = 1024;
+hipError_t launch_check_mask(const uint8_t* mask, int64_t n, int32_t* bad, int n_wg, hipStream_t stream);
+
 struct AttnArgs {
   const uint16_t* q;
   const uint16_t* k;

@@ -34,7 +34,26 @@ __global__ __launch_bounds__(256) void compact_kernel(const uint8_t* __restrict_
   if (lane == 0) kv_cnt[row] = static_cast<int32_t>(base);
 }
 
+// Mask value check ("Mask Requirements": entries are 0 or 1). Workgroup w
+// writes bad[w] = 1 if any byte it scanned is neither 0 nor 1, else 0: every
+// slot is written by exactly one workgroup, so no zeroing pass and no atomics.
+__global__ __launch_bounds__(256) void check_mask_kernel(const uint8_t* __restrict__ mask, int64_t n,
+                                                         int32_t* __restrict__ bad) {
+  int found = 0;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
+    found |= mask[i] > 1;
+  found = __syncthreads_or(found);
+  if (threadIdx.x == 0) bad[blockIdx.x] = found ? 1 : 0;
+}
+
 }  // namespace
+
+hipError_t launch_check_mask(const uint8_t* mask, int64_t n, int32_t* bad, int n_wg, hipStream_t stream) {
+  void* args[] = {(void*)&mask, (void*)&n, (void*)&bad};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&check_mask_kernel), dim3(static_cast<uint32_t>(n_wg)),
+                         dim3(256), args, 0, stream);
+}
 
 hipError_t launch_compact(const uint8_t* mask, int64_t rows, int64_t n_kb, int32_t* kv_idx,
                           int32_t* kv_cnt, hipStream_t stream) {

@@ -66,7 +66,8 @@ extern "C" {
 #define SPARGE_ERR_ALIAS -5      /* an output range overlaps an input range */
 #define SPARGE_ERR_WORKSPACE -6  /* workspace NULL or smaller than sparge_workspace_bytes() */
 #define SPARGE_ERR_ARG -7        /* another invalid argument (e.g. block_rows not 64/128) */
-#define SPARGE_ERR_LAUNCH -8     /* the HIP runtime rejected a kernel launch */
+#define SPARGE_ERR_LAUNCH -8     /* the HIP runtime rejected a kernel launch (or a copy or synchronisation failed) */
+#define SPARGE_ERR_MASK_VALUE -9 /* (checking calls only) a mask_id byte is neither 0 nor 1 */
 
 /* Query rows per query block and key rows per key block
  * (SpargeAttention Documentation, "Mask Requirements": fixed 128x64 blocks). */
@@ -93,7 +94,10 @@ int sparge_topk_count(int64_t n_kblocks, double topk, int64_t *k_out);
  * (dense attention needs no workspace, but the call accepts any workspace). */
 size_t sparge_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, double topk);
 
-/* Block-mean pooling (first step of mask prediction).
+/* Block-mean pooling, the first step of mask prediction: the "mean" of the
+ * top-k API's meansim selection (SpargeAttention Documentation, the paragraph
+ * on spas_sage2_attn_meansim_topk_cuda), over the 128-row query blocks and
+ * 64-row key blocks of the mask (same page, "Mask Requirements").
  *   x          (B, H, N, D) bf16, strides x_strides (elements, B/H/N axes).
  *   block_rows 128 for Q, 64 for K.
  *   out        (B, H, ceil(N/block_rows), D) fp32, contiguous. Row i is the
@@ -103,7 +107,11 @@ size_t sparge_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, double
 int sparge_pool_blocks(const uint16_t *x, int64_t B, int64_t H, int64_t N, int64_t D,
                        const int64_t x_strides[3], int block_rows, float *out, void *stream);
 
-/* Pooled-block scoring and per-row top-k selection.
+/* Pooled-block scoring and per-row top-k selection: the "sim" and "topk" of
+ * the same API (SpargeAttention Documentation, the paragraph on
+ * spas_sage2_attn_meansim_topk_cuda: topk is the share of key blocks kept,
+ * higher favouring accuracy), producing the block mask of "Mask Requirements"
+ * (shape (B, H, ceil(N/128), ceil(N/64)), entries 0 or 1).
  *   qbar     (B, H, N_QB, D) fp32 contiguous (sparge_pool_blocks with 128).
  *   kbar     (B, H, N_KB, D) fp32 contiguous (sparge_pool_blocks with 64).
  *   topk     in (0, 1]; each row keeps k = sparge_topk_count(N_KB, topk) blocks
@@ -165,6 +173,30 @@ int block_sparse_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                       int64_t D, const int64_t q_strides[3], const int64_t k_strides[3],
                       const int64_t v_strides[3], const int64_t o_strides[3], float scale,
                       int is_causal, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Mask value check (SpargeAttention Documentation, "Mask Requirements": the
+ * mask consists of 0 and 1 entries). Scans every byte of mask_id
+ * ((B, H, N_QB, N_KB) uint8 contiguous) on the device and returns SPARGE_OK if
+ * all are 0 or 1, SPARGE_ERR_MASK_VALUE otherwise. Unlike the other calls it
+ * SYNCHRONISES `stream` (it reads the result back), so it is for debugging and
+ * input validation, not for graph capture.
+ *   workspace   device scratch of at least sparge_workspace_bytes(B, H, N, 64, -1)
+ *               bytes (it uses 4 bytes per 256 mask bytes, at most 4 KiB).
+ * Errors: NULL, SHAPE, WORKSPACE, ALIAS (workspace overlapping the mask), LAUNCH, MASK_VALUE. */
+int sparge_check_mask(const uint8_t *mask_id, int64_t B, int64_t H, int64_t N, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/* block_sparse_attn with its mask checked first: sparge_check_mask, then (only
+ * if every byte is 0 or 1) block_sparse_attn with the same arguments. A mask
+ * with another value is rejected with SPARGE_ERR_MASK_VALUE and nothing is
+ * computed; the fast call instead counts any nonzero byte as 1. Synchronises
+ * `stream` when mask_id is not NULL.
+ * Errors: those of block_sparse_attn, plus MASK_VALUE. */
+int block_sparse_attn_checked(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                              const uint8_t *mask_id, uint16_t *out, int64_t B, int64_t H, int64_t N,
+                              int64_t D, const int64_t q_strides[3], const int64_t k_strides[3],
+                              const int64_t v_strides[3], const int64_t o_strides[3], float scale,
+                              int is_causal, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Top-k block-sparse attention, a drop-in for scaled dot-product attention
  * (SpargeAttention Documentation, spas_sage2_attn_meansim_topk_cuda: higher

@@ -298,6 +298,40 @@ def masked_attention_rows(q_h, k_h, v_h, mask_h, rows, scale: float | None = Non
     return out
 
 
+def masked_attention_sampled(q_h, k_h, v_h, mask_h, rows, scale: float | None = None,
+                             causal: bool = False, chunk: int = 256) -> np.ndarray:
+    """Outputs of scattered query rows of one head, each row on its own.
+
+    The same quantity as masked_attention_rows, written as a masked softmax
+    over the whole key axis: row r scores every key, keys outside the blocks
+    its query block selects (and, with causal=True, keys after r) get weight
+    zero, and the rest are normalised as usual. A row with no such key outputs
+    zeros. Rows are handled in groups of `chunk` only to bound memory.
+    q_h, k_h, v_h (N, D); mask_h (Qb, Kb); rows: token indices.
+    """
+    q_h = np.asarray(q_h, dtype=np.float64)
+    k_h = np.asarray(k_h, dtype=np.float64)
+    v_h = np.asarray(v_h, dtype=np.float64)
+    mask_h = np.asarray(mask_h)
+    N, D = q_h.shape
+    scale = default_scale(D) if scale is None else float(scale)
+    rows = np.asarray(rows, dtype=np.int64)
+    key_block = np.arange(N) // K_BLOCK
+    out = np.zeros((rows.shape[0], D), dtype=np.float64)
+    for lo in range(0, rows.shape[0], chunk):
+        r = rows[lo:lo + chunk]
+        kept = mask_h[r // Q_BLOCK][:, key_block] != 0
+        if causal:
+            kept &= np.arange(N)[None, :] <= r[:, None]
+        logits = np.where(kept, scale * (q_h[r] @ k_h.T), -np.inf)
+        any_key = kept.any(axis=1)
+        top = np.where(any_key, logits.max(axis=1), 0.0)
+        w = np.exp(logits - top[:, None])
+        den = np.where(any_key, w.sum(axis=1), 1.0)
+        out[lo:lo + r.shape[0]] = (w @ v_h) / den[:, None]
+    return out
+
+
 def compact_mask(mask: np.ndarray):
     """Per row, the ascending list of selected key-block ids and its length.
 

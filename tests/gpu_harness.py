@@ -3,6 +3,9 @@ compare device results with the CPU oracle. Nothing here computes any step of
 the method."""
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -59,3 +62,19 @@ def oracle_mask_parity(q64_heads, k64_heads, topk, mask_dev, scale=None, causal=
             for key in tot:
                 tot[key] += rep.get(key, 0)
     return tot
+
+
+def host_threads() -> int:
+    """Worker threads for oracle work: the host CPUs this process may use, at most 16."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def parallel_heads(fn, heads):
+    """fn(b, h) for every (b, h), on host threads with single-threaded BLAS in each.
+
+    The oracle's per-head work is independent, so the heads are spread over the
+    host cores; returns the results in the order of `heads`."""
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        with ThreadPoolExecutor(max_workers=host_threads()) as ex:
+            return list(ex.map(lambda bh: fn(*bh), heads))

@@ -13,7 +13,7 @@ import oracle
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sparge.h")
 
-OK, NULL, SHAPE, TOPK, STRIDE, ALIAS, WORKSPACE, ARG = 0, -1, -2, -3, -4, -5, -6, -7
+OK, NULL, SHAPE, TOPK, STRIDE, ALIAS, WORKSPACE, ARG, MASK_VALUE = 0, -1, -2, -3, -4, -5, -6, -7, -9
 
 
 def declared_functions():
@@ -38,8 +38,9 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in (OK, NULL, SHAPE, TOPK, STRIDE, ALIAS, WORKSPACE, ARG, -8, 12345):
+    for code in (OK, NULL, SHAPE, TOPK, STRIDE, ALIAS, WORKSPACE, ARG, -8, MASK_VALUE, 12345):
         assert lib.sparge_status_string(code)
+    assert b"0 or 1" in lib.sparge_status_string(MASK_VALUE)
 
 
 def test_topk_count_matches_oracle_and_golden(lib):
@@ -88,13 +89,16 @@ def attn_call(lib, fn, q=A, k=Bp, v=C, out=O, B=1, H=2, N=256, D=64, qs=None, ks
     if fn == "topk":
         return lib.sparge_attn_topk(q, k, v, topk, out, B, H, N, D, qs, ks, vs, os_, 0.0, causal, mask,
                                     ws, wsb, None)
+    if fn == "checked":
+        return lib.block_sparse_attn_checked(q, k, v, mask, out, B, H, N, D, qs, ks, vs, os_, 0.0, causal,
+                                             ws, wsb, None)
     return lib.block_sparse_attn(q, k, v, mask, out, B, H, N, D, qs, ks, vs, os_, 0.0, causal, ws, wsb,
                                  None)
 
 
-@pytest.mark.parametrize("fn", ["topk", "mask"])
+@pytest.mark.parametrize("fn", ["topk", "mask", "checked"])
 def test_attention_argument_errors(lib, fn):
-    mask = M if fn == "mask" else None
+    mask = None if fn == "topk" else M
     assert attn_call(lib, fn, q=None, mask=mask) == NULL
     assert attn_call(lib, fn, out=None, mask=mask) == NULL
     assert attn_call(lib, fn, D=96, mask=mask) == SHAPE
@@ -124,6 +128,21 @@ def test_attention_argument_errors(lib, fn):
     else:
         assert attn_call(lib, fn, mask=O + 64, ws=W, wsb=need) == ALIAS                 # mask inside out
         assert attn_call(lib, fn, mask=W + 64, ws=W, wsb=need) == ALIAS                 # mask inside workspace
+
+
+def test_check_mask_errors(lib):
+    # every rejection happens on the host, before the device scan
+    assert lib.sparge_check_mask(None, 1, 2, 256, W, 4096, None) == NULL
+    assert lib.sparge_check_mask(M, 1, 0, 256, W, 4096, None) == SHAPE
+    assert lib.sparge_check_mask(M, 1, 2, 256, None, 4096, None) == WORKSPACE
+    assert lib.sparge_check_mask(M, 1, 2, 256, W, 0, None) == WORKSPACE       # needs 4 bytes (16 mask bytes)
+    assert lib.sparge_check_mask(M, 1, 2, 256, W + 4, 4096, None) == WORKSPACE   # misaligned
+    assert lib.sparge_check_mask(M, 1, 2, 256, M, 4096, None) == ALIAS
+    # the workspace the checking attention call needs also holds the flags
+    for n in (1, 63, 256, 75600):
+        rows, kb = -(-n // 128), -(-n // 64)
+        flags = 4 * min(1024, -(-(rows * kb) // 256))
+        assert sp.workspace_bytes(1, 1, n, 64) >= flags
 
 
 def test_pool_predict_compact_errors(lib):

@@ -25,7 +25,8 @@ def _ns(**over):
              "block_logits", "row_softmax", "select_topk", "predict_mask", "selected_keys",
              "attend_rows", "masked_attention", "masked_attention_rows", "compact_mask", "mask_parity",
              "causal_key_blocks", "cube_permutation", "morton_code", "morton_permutation",
-             "permute_tokens", "select_cdf", "predict_mask_cdf", "mask_parity_cdf"]
+             "permute_tokens", "select_cdf", "predict_mask_cdf", "mask_parity_cdf",
+             "masked_attention_sampled"]
     d = {n: getattr(real_oracle, n) for n in names}
     d.update(over)
     return types.SimpleNamespace(**d)
@@ -253,6 +254,47 @@ def pin_attention_rows(o):
     assert np.abs(got - ref).max() <= 1e-12
 
 
+def pin_attention_sampled(o):
+    """Scattered rows, each against torch SDPA in float64 with the token-level mask."""
+    rng = np.random.default_rng(18)
+    for n, d in ((333, 8), (200, 16)):
+        q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+        qb, kb = -(-n // 128), -(-n // 64)
+        m = (rng.random((qb, kb)) < 0.5).astype(np.uint8)
+        m[:, kb - 1] = 1
+        rows = np.array(sorted({0, 5, 127, 128, min(n - 1, 255), n - 1, n // 2}))
+        sc = 1 / math.sqrt(d)
+        ref = _sdpa(q[None, None], k[None, None], v[None, None], sc, _expand(m, n))[0, 0][rows]
+        got = o.masked_attention_sampled(q, k, v, m, rows, chunk=3)
+        assert np.abs(got - ref).max() <= 1e-12
+        assert np.abs(got - o.masked_attention_rows(q, k, v, m, rows)).max() <= 1e-12
+        # an explicit scale, and rows given in any order
+        perm = rows[::-1]
+        got = o.masked_attention_sampled(q, k, v, m, perm, scale=0.3)
+        ref = _sdpa(q[None, None], k[None, None], v[None, None], 0.3, _expand(m, n))[0, 0][perm]
+        assert np.abs(got - ref).max() <= 1e-12
+        # causal: the token mask AND the lower triangle; a row whose kept keys all
+        # lie after it outputs zeros
+        mc = m.copy()
+        mc[0] = 0
+        mc[0, 1] = 1                                    # block 0 sees only keys 64..127
+        tok = _expand(mc, n) & np.tril(np.ones((n, n), dtype=bool))
+        got = o.masked_attention_sampled(q, k, v, mc, rows, causal=True)
+        for i, r in enumerate(rows):
+            if tok[r].any():
+                ref = _sdpa(q[None, None, r:r + 1], k[None, None], v[None, None], sc,
+                            tok[None, None, r:r + 1])[0, 0, 0]
+                assert np.abs(got[i] - ref).max() <= 1e-12
+            else:
+                assert (got[i] == 0).all()
+        assert (got[0] == 0).all() and (got[1] == 0).all()   # rows 0 and 5 see no kept key
+        # an empty mask row outputs zeros
+        me = m.copy()
+        me[1] = 0
+        got = o.masked_attention_sampled(q, k, v, me, np.array([128, min(n - 1, 200)]))
+        assert (got == 0).all()
+
+
 def pin_compact(o):
     rng = np.random.default_rng(9)
     m = (rng.random((2, 3, 9)) < 0.4).astype(np.uint8)
@@ -466,7 +508,8 @@ def pin_cdf_select(o):
 
 PINS = [pin_block_counts, pin_topk_count, pin_pool, pin_scores, pin_select, pin_predict,
         pin_predict_ties, pin_attention, pin_attention_closed_forms, pin_attention_rows,
-        pin_compact, pin_mask_parity, pin_causal_attention, pin_causal_predict, pin_token_layouts, pin_cdf_select]
+        pin_compact, pin_mask_parity, pin_causal_attention, pin_causal_predict, pin_token_layouts, pin_cdf_select,
+        pin_attention_sampled]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -515,6 +558,29 @@ def _broken_variants():
         if not (0 < topk <= 1):
             raise ValueError
         return max(1, min(kb, math.ceil(topk * kb)))
+
+    def sampled_wrong_block(q_h, k_h, v_h, mask_h, rows, scale=None, causal=False, chunk=256):
+        rows = np.asarray(rows)
+        out = np.empty((rows.size, np.asarray(q_h).shape[1]))
+        for i, r in enumerate(rows):
+            m = np.zeros_like(np.asarray(mask_h))
+            m[r // 128] = np.asarray(mask_h)[min(r // 64, m.shape[0] - 1)]
+            out[i] = o.masked_attention_rows(q_h, k_h, v_h, m, [r], scale, causal)[0]
+        return out
+
+    def sampled_strict_causal(q_h, k_h, v_h, mask_h, rows, scale=None, causal=False, chunk=256):
+        # the causal test written as c < r instead of c <= r
+        q_h, k_h, v_h = (np.asarray(a, dtype=np.float64) for a in (q_h, k_h, v_h))
+        n, d = q_h.shape
+        sc = 1 / math.sqrt(d) if scale is None else scale
+        rows = np.asarray(rows)
+        kept = np.asarray(mask_h)[rows // 128][:, np.arange(n) // 64] != 0
+        if causal:
+            kept &= np.arange(n)[None, :] < rows[:, None]
+        lg = np.where(kept, sc * (q_h[rows] @ k_h.T), -np.inf)
+        anyk = kept.any(1)
+        w = np.exp(lg - np.where(anyk, lg.max(1), 0.0)[:, None])
+        return (w @ v_h) / np.where(anyk, w.sum(1), 1.0)[:, None]
 
     def attend_no_scale(qr, ks, vs, scale, rows=None, cols=None):
         return o.attend_rows(qr, ks, vs, 1.0, rows, cols)
@@ -638,6 +704,8 @@ def _broken_variants():
         "attention without normalisation": dict(attend_rows=attend_unnormalised),
         "key blocks of 128 rows": dict(selected_keys=selected_keys_wrong_block),
         "ragged last key block dropped": dict(selected_keys=selected_keys_drop_tail),
+        "sampled rows take the mask row of the 64-row block": dict(masked_attention_sampled=sampled_wrong_block),
+        "sampled causal rows exclude their own key": dict(masked_attention_sampled=sampled_strict_causal),
         "K used in place of V": dict(attend_rows=attend_transposed_v),
         "parity without the near-tie band": dict(mask_parity=parity_no_band),
         "causal row does not see its own key": dict(attend_rows=attend_causal_strict),
