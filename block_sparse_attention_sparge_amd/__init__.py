@@ -90,6 +90,8 @@ def load_library() -> ctypes.CDLL:
                                  ci, vp, vp, sz, vp]),
         "sparge_permute_tokens": (ci, [vp, vp, vp, i64, i64, i64, i64, s3, s3, ci, vp]),
         "sparge_check_mask": (ci, [vp, i64, i64, i64, vp, sz, vp]),
+        "sparge_attn_topk_noalloc": (ci, [vp, vp, vp, f64, vp, i64, i64, i64, i64, s3, s3, s3, s3, f32,
+                                          ci, vp, vp]),
         "block_sparse_attn_checked": (ci, [vp, vp, vp, vp, vp, i64, i64, i64, i64, s3, s3, s3, s3, f32,
                                            ci, vp, sz, vp]),
     }

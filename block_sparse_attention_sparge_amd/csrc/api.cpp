@@ -171,6 +171,7 @@ const char* sparge_status_string(int status) {
     case SPARGE_ERR_ARG: return "invalid argument";
     case SPARGE_ERR_LAUNCH: return "kernel launch failed";
     case SPARGE_ERR_MASK_VALUE: return "mask_id holds a value other than 0 or 1";
+    case SPARGE_ERR_SCRATCH_LIMIT: return "the shape needs more workspace than the no-allocation call's fixed 128 MiB array";
     default: return "unknown status";
   }
 }
@@ -366,20 +367,20 @@ int sparge_attn_topk(const uint16_t* q, const uint16_t* k, const uint16_t* v, do
   if (N > SPARGE_MAX_PREDICT_N) return SPARGE_ERR_SHAPE;
   int64_t kk = 0;
   if (int rc = topk_count(n_kblocks(N), topk, &kk)) return rc;
-  const TopkWs w = topk_layout(B, H, N, D, kk);
-  if (!workspace || workspace_bytes < w.total || !aligned16(workspace)) return SPARGE_ERR_WORKSPACE;
   const size_t rows = static_cast<size_t>(B * H * n_qblocks(N));
-  const Range rw = range_bytes(workspace, w.total);
   const Range ro = range_bf16(out, B, H, N, D, o_strides);
   const Range rq = range_bf16(q, B, H, N, D, q_strides);
   const Range rk = range_bf16(k, B, H, N, D, k_strides);
   const Range rv = range_bf16(v, B, H, N, D, v_strides);
-  if (overlap(rw, ro) || overlap(rw, rq) || overlap(rw, rk) || overlap(rw, rv)) return SPARGE_ERR_ALIAS;
-  if (mask_out) {
-    const Range rm = range_bytes(mask_out, rows * n_kblocks(N));
-    if (overlap(rm, ro) || overlap(rm, rw) || overlap(rm, rq) || overlap(rm, rk) || overlap(rm, rv))
-      return SPARGE_ERR_ALIAS;
-  }
+  const Range rm = mask_out ? range_bytes(mask_out, rows * n_kblocks(N)) : Range{0, 0};
+  if (mask_out && (overlap(rm, ro) || overlap(rm, rq) || overlap(rm, rk) || overlap(rm, rv)))
+    return SPARGE_ERR_ALIAS;
+  // the workspace comes last: every check before it concerns the caller's own buffers
+  const TopkWs w = topk_layout(B, H, N, D, kk);
+  if (!workspace || workspace_bytes < w.total || !aligned16(workspace)) return SPARGE_ERR_WORKSPACE;
+  const Range rw = range_bytes(workspace, w.total);
+  if (overlap(rw, ro) || overlap(rw, rq) || overlap(rw, rk) || overlap(rw, rv) || overlap(rw, rm))
+    return SPARGE_ERR_ALIAS;
 
   const float sc = resolve_scale(scale, D);
   const hipStream_t st = static_cast<hipStream_t>(stream);

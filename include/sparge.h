@@ -68,6 +68,7 @@ extern "C" {
 #define SPARGE_ERR_ARG -7        /* another invalid argument (e.g. block_rows not 64/128) */
 #define SPARGE_ERR_LAUNCH -8     /* the HIP runtime rejected a kernel launch (or a copy or synchronisation failed) */
 #define SPARGE_ERR_MASK_VALUE -9 /* (checking calls only) a mask_id byte is neither 0 nor 1 */
+#define SPARGE_ERR_SCRATCH_LIMIT -10 /* (no-allocation call) the shape needs more workspace than its fixed array */
 
 /* Query rows per query block and key rows per key block
  * (SpargeAttention Documentation, "Mask Requirements": fixed 128x64 blocks). */
@@ -214,6 +215,31 @@ int sparge_attn_topk(const uint16_t *q, const uint16_t *k, const uint16_t *v, do
                      const int64_t v_strides[3], const int64_t o_strides[3], float scale,
                      int is_causal, uint8_t *mask_out, void *workspace, size_t workspace_bytes,
                      void *stream);
+
+/* Bytes of the fixed device array that sparge_attn_topk_noalloc uses as its
+ * workspace (one array per GPU, held from library load until the process ends). */
+#define SPARGE_NOALLOC_SCRATCH_BYTES (128u << 20)
+
+/* sparge_attn_topk for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same computation and arguments, without the workspace arguments. Its
+ * workspace is a fixed SPARGE_NOALLOC_SCRATCH_BYTES array in device memory,
+ * one per GPU, resolved on the first call on each device; the call itself
+ * allocates nothing. The caller still passes inputs and outputs.
+ *   A shape whose workspace (sparge_workspace_bytes(B, H, N, D, topk)) exceeds
+ *   the array is refused with SPARGE_ERR_SCRATCH_LIMIT before any HIP call
+ *   (128 MiB covers, e.g., B=1, H=40, N=75600, D=128 up to topk 0.874).
+ *   All calls on one GPU share its array and each call overwrites it: calls
+ *   that may overlap on one GPU (different streams, or several host threads)
+ *   race and must be serialised by the caller. The stream must belong to the
+ *   current device.
+ * Errors: those of sparge_attn_topk except WORKSPACE, plus SCRATCH_LIMIT;
+ * LAUNCH also if the array's device address cannot be resolved. */
+int sparge_attn_topk_noalloc(const uint16_t *q, const uint16_t *k, const uint16_t *v, double topk,
+                             uint16_t *out, int64_t B, int64_t H, int64_t N, int64_t D,
+                             const int64_t q_strides[3], const int64_t k_strides[3],
+                             const int64_t v_strides[3], const int64_t o_strides[3], float scale,
+                             int is_causal, uint8_t *mask_out, void *stream);
 
 /* CDF-threshold selection (the inference scripts' "cdfthreshd" mode, SpargeAttention
  * Documentation, output-directory list; the pages give only the name and a

@@ -212,3 +212,26 @@ def test_python_wrapper_rejects_without_gpu():
     with pytest.raises(ValueError):
         sp.attn_topk(x, x, x)          # CPU tensor
     assert sp.mask_shape(1, 2, 75600) == (1, 2, 591, 1182)
+
+
+def test_noalloc_scratch_limit(lib):
+    """The no-allocation call refuses a shape whose workspace exceeds its fixed
+    array on the host, before any HIP call (fake addresses, never dereferenced)."""
+    assert sp.workspace_bytes(1, 40, 75600, 128, 0.9) > 128 << 20
+    st = S(40 * 75600 * 128, 75600 * 128, 128)
+    g = [0x40000000 * i for i in range(1, 5)]       # 1 GiB apart: the 774 MB operands do not overlap
+    assert lib.sparge_attn_topk_noalloc(g[0], g[1], g[2], 0.9, g[3], 1, 40, 75600, 128, st, st, st, st, 0.0, 0,
+                                        None, None) == -10
+    # invalid arguments are reported by the regular call's checks
+    assert lib.sparge_attn_topk_noalloc(A, Bp, C, 1.5, O, 1, 2, 256, 64, contiguous(2, 256, 64),
+                                        contiguous(2, 256, 64), contiguous(2, 256, 64),
+                                        contiguous(2, 256, 64), 0.0, 0, None, None) == TOPK
+    assert lib.sparge_attn_topk_noalloc(None, Bp, C, 0.5, O, 1, 2, 256, 64, contiguous(2, 256, 64),
+                                        contiguous(2, 256, 64), contiguous(2, 256, 64),
+                                        contiguous(2, 256, 64), 0.0, 0, None, None) == NULL
+    assert lib.sparge_attn_topk_noalloc(A, Bp, C, 0.5, A + 64, 1, 2, 256, 64, contiguous(2, 256, 64),
+                                        contiguous(2, 256, 64), contiguous(2, 256, 64),
+                                        contiguous(2, 256, 64), 0.0, 0, None, None) == ALIAS
+    assert lib.sparge_attn_topk_noalloc(A, Bp, C, 0.5, O, 1, 2, 256, 64, contiguous(2, 256, 64),
+                                        contiguous(2, 256, 64), contiguous(2, 256, 64),
+                                        contiguous(2, 256, 64), 0.0, 0, A + 64, None) == ALIAS  # mask in q
