@@ -17,7 +17,7 @@
 //   laid out as the B operand of O^T += V^T P^T, so they never leave registers.
 //   V^T operands come straight from the row-major V tile through the gfx950
 //   transpose read ds_read_b64_tr_b16. K rows are read in a permuted order
-//   (sigma below) so that the S^T accumulators hold consecutive keys, which is
+//   (sigma in attn_geometry.h) so that the S^T accumulators hold consecutive keys, which is
 //   the key order the PV operands need.
 //
 // Softmax
@@ -47,6 +47,7 @@
 //   cache and neighbouring query blocks, whose lists overlap, share L2.
 #include <type_traits>
 
+#include "attn_geometry.h"
 #include "common.h"
 
 namespace sparge {
@@ -69,23 +70,9 @@ constexpr int kBufferFlags = 0x00020000;
 constexpr int kSchedKeepLoads = 0x0506;
 
 template <int D>
-struct Cfg {
-  static constexpr int kRowBytes = D * 2;
-  static constexpr int kChunks = D / 8;                     // 16-byte chunks per row
-  static constexpr int kTile = kKBlock * kRowBytes;         // one K or V tile in LDS
-  static constexpr int kStage = 2 * kTile;                  // K tile then V tile
-  static constexpr int kLds = 2 * kStage;                   // double buffered
-  static constexpr int kRowsPerInst = 64 / kChunks;         // rows one wavefront load fills
-  static constexpr int kInstPerWave = kKBlock / (4 * kRowsPerInst);
-  static constexpr int kSteps = D / 16;                     // k-steps of QK^T
-  static constexpr int kDChunks = D / 32;                   // 32-column chunks of O
+struct Cfg : geom::Tile<D> {
+  static constexpr int kTile = geom::Tile<D>::kBytes;       // one K or V tile in LDS
 };
-
-// Chunk swizzles (XOR on the 16-byte chunk index within a row).
-template <int D>
-__device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
-template <int D>
-__device__ __forceinline__ int swz_v(int r) { return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2); }
 
 struct Params {
   const uint16_t* q;
@@ -101,13 +88,6 @@ struct Params {
   Strides qs, ks, vs, os;
   float c;             // scale * log2(e)
 };
-
-// Row of the K tile that feeds A-operand row m, chosen so that accumulator
-// register i of lane (n, g) holds key 8g + i (i < 8) or 16 + 8g + (i - 8).
-__device__ __forceinline__ int sigma(int m) {
-  const int a = m >> 3, gg = (m >> 2) & 1, bb = m & 3;
-  return 16 * (a >> 1) + 8 * gg + 4 * (a & 1) + bb;
-}
 
 // Key block visited at step tt. An id outside [0, n_kb) maps to a block past
 // the end of the sequence whose keys are all masked, so a corrupt list entry
@@ -207,21 +187,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   float m = -INFINITY;
   float l = 0.f;
 
-  // ---- per-lane LDS geometry (constant over the walk)
-  // K A-operand: row sigma(n) (+32 for the second half), logical chunk 2s + g.
-  const int krow = sigma(n);
-  const int kx = swz_k<D>(krow);
+  // ---- per-lane LDS geometry (constant over the walk; see attn_geometry.h)
   int koff[C::kSteps];
 #pragma unroll
-  for (int s = 0; s < C::kSteps; ++s) koff[s] = krow * C::kRowBytes + 16 * ((2 * s + g) ^ kx);
-  // V transpose read: row 16u + 8g + 4r + (lane%16)/4, logical chunk 4cc + lcx, half (lane & 1).
-  const int vrow = 8 * g + ((lane & 15) >> 2);
-  const int vx = swz_v<D>(vrow);
-  const int lcx = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  for (int s = 0; s < C::kSteps; ++s) koff[s] = geom::k_read<D>(n, g, s);
   int voff[C::kDChunks];
 #pragma unroll
-  for (int cc = 0; cc < C::kDChunks; ++cc)
-    voff[cc] = vrow * C::kRowBytes + 16 * ((4 * cc + lcx) ^ vx) + 8 * (lane & 1);
+  for (int cc = 0; cc < C::kDChunks; ++cc) voff[cc] = geom::v_read<D>(lane, cc);
 
   // ---- global -> LDS: wavefront load e fills rows [r0, r0 + kRowsPerInst) of a tile.
   // Loads go through a buffer resource per tile (scalar base and byte bound) with
@@ -231,11 +203,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   uint32_t ld_koff[C::kInstPerWave], ld_voff[C::kInstPerWave];
 #pragma unroll
   for (int e = 0; e < C::kInstPerWave; ++e) {
-    const int inst = wave * C::kInstPerWave + e;
-    const int r = inst * C::kRowsPerInst + lane / C::kChunks;
-    const int pc = lane % C::kChunks;
-    ld_koff[e] = static_cast<uint32_t>((r * p.ks.n + 8 * (pc ^ swz_k<D>(r))) * 2);
-    ld_voff[e] = static_cast<uint32_t>((r * p.vs.n + 8 * (pc ^ swz_v<D>(r))) * 2);
+    ld_koff[e] = geom::load_offset<D, false>(wave, e, lane, p.ks.n);
+    ld_voff[e] = geom::load_offset<D, true>(wave, e, lane, p.vs.n);
   }
   // Tile j of an operand starts j * tile_bytes past its head; its bound is the
   // whole tile, the rows left at the sequence end, or nothing (j past the end).
@@ -245,14 +214,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   const uint32_t k_tail = static_cast<uint32_t>((p.N - n_full * kKBlock) * p.ks.n * 2);
   const uint32_t v_tail = static_cast<uint32_t>((p.N - n_full * kKBlock) * p.vs.n * 2);
   auto tile_rsrc = [&](const uint16_t* base, int64_t j, uint32_t tile_bytes, uint32_t tail_bytes) {
-    const uint32_t bound = j < n_full ? tile_bytes : (j == n_full ? tail_bytes : 0u);
+    const uint32_t bound = geom::tile_bound(j, n_full, tile_bytes, tail_bytes);
     const char* ptr = reinterpret_cast<const char*>(base) +
                       static_cast<uint64_t>(static_cast<uint32_t>(j)) * tile_bytes;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(ptr), static_cast<short>(0),
                                              static_cast<int>(bound), kBufferFlags);
   };
   auto issue_one = [&](__amdgpu_buffer_rsrc_t rs, uint32_t off, char* buf, int e) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + (wave_s * C::kInstPerWave + e) * 1024),
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + geom::load_lds<D>(wave_s, e)),
                                              16, static_cast<int>(off), 0, 0, 0);
   };
   // Pins a load between the MFMAs around it: VALU, SALU, transcendental and
