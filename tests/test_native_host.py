@@ -60,8 +60,10 @@ def test_address_replay_catches_planted_mistakes(replay, plant):
 
 def test_sanitized_host_abi(tmp_path):
     """ASan + UBSan on the library's host code; device code built as usual."""
+    from block_sparse_attention_sparge_amd.build import SOURCES
     build = os.path.join(ROOT, "_build")
-    objs = [os.path.join(build, s) for s in ("pool.o", "predict.o", "compact.o", "attn_fwd.o", "permute.o")]
+    sanitized = ("api.cpp", "noalloc.hip")          # the library's host code, built below
+    objs = [os.path.join(build, os.path.splitext(s)[0] + ".o") for s in SOURCES if s not in sanitized]
     if not all(os.path.exists(o) for o in objs):
         from block_sparse_attention_sparge_amd.build import build as build_lib
         build_lib(verbose=False)
@@ -70,7 +72,7 @@ def test_sanitized_host_abi(tmp_path):
     common = ["-std=c++17", "-O1", "-g", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
               "-I", os.path.join(ROOT, "include")]
     out_objs = []
-    for src in ("api.cpp", "noalloc.hip"):
+    for src in sanitized:
         obj = str(tmp_path / (src + ".o"))
         rc, out = _run([HIPCC] + common + ["-fPIC", "-x", "hip", "--offload-arch=gfx950"] + san +
                        ["-c", os.path.join(CSRC, src), "-o", obj])
