@@ -53,6 +53,24 @@ __device__ __forceinline__ uint32_t count_below(uint64_t m) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
 }
 
+// Workgroup -> (head bh, group of query blocks). Consecutive workgroup ids go
+// to consecutive XCDs. With `deal`, every group of a head runs on one XCD, so
+// the head's pooled keys are fetched into one L2 instead of all eight; the
+// grid then covers a multiple of 8 heads and ids past the last head get
+// bh = BH (nothing to do).
+__device__ __forceinline__ void work_item(int64_t n_groups, int64_t BH, int deal, int64_t& bh, int64_t& group) {
+  const int64_t w = blockIdx.x;
+  if (deal) {
+    const int64_t it = w / kNumXcd;
+    bh = (it / n_groups) * kNumXcd + (w - (w / kNumXcd) * kNumXcd);
+    group = it - (it / n_groups) * n_groups;
+    if (bh > BH) bh = BH;
+  } else {
+    bh = w / n_groups;
+    group = w - bh * n_groups;
+  }
+}
+
 // Writes the fp32 scores of the R pooled query rows of a group (rows past the
 // last query block repeat it; their scores are never read) against every key
 // block of the head to sc. The query rows are wavefront-uniform, so they are
@@ -106,21 +124,24 @@ __device__ __forceinline__ int64_t candidates(int causal, int64_t qi, int64_t N,
 template <int D, int R>
 __global__ __launch_bounds__(kThreads) void predict_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, int64_t N, int64_t n_qb,
-    int64_t n_kb, int64_t n_groups, int64_t k, double topk, int causal, float scale,
+    int64_t n_kb, int64_t n_groups, int64_t BH, int deal, int64_t k, double topk, int causal, float scale,
     uint8_t* __restrict__ mask, int32_t* __restrict__ kv_idx, int32_t* __restrict__ kv_cnt) {
   extern __shared__ float4 smem4[];
   float* sc = reinterpret_cast<float*>(smem4);             // [R][n_kb]
   uint32_t* hist = reinterpret_cast<uint32_t*>(sc + R * n_kb);   // [kWaves][256]
 
-  const int64_t bh = blockIdx.x / n_groups;
-  const int64_t row0 = (blockIdx.x - bh * n_groups) * R;   // first query block of this group
+  int64_t bh, group;
+  work_item(n_groups, BH, deal, bh, group);
+  if (bh >= BH) return;
+  const int64_t row0 = group * R;   // first query block of this group
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
   pooled_scores<D, R>(qbar, kbar, bh, row0, n_qb, n_kb, scale, sc);
 
-  // Selection: wavefront `wave` takes rows wave, wave + 4, ...; every wavefront
-  // runs the same number of rounds so the block-wide barriers stay uniform.
+  // Selection: wavefront `wave` takes row `wave` of the group (R <= kWaves, so
+  // one round; wavefronts past R or past the last query block only join the
+  // barriers). Every wavefront runs the same rounds so the barriers stay uniform.
   uint32_t* h = hist + wave * 256;
   constexpr int kRounds = (R + kWaves - 1) / kWaves;
   for (int round = 0; round < kRounds; ++round) {
@@ -237,15 +258,17 @@ constexpr float kFixedOne = 2147483648.0f;   // weights in units of 2^-31
 template <int D, int R>
 __global__ __launch_bounds__(kThreads) void predict_cdf_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, int64_t N, int64_t n_qb,
-    int64_t n_kb, int64_t n_groups, double tau, int causal, float scale,
+    int64_t n_kb, int64_t n_groups, int64_t BH, int deal, double tau, int causal, float scale,
     uint8_t* __restrict__ mask, int32_t* __restrict__ kv_idx, int32_t* __restrict__ kv_cnt) {
   extern __shared__ float4 smem4[];
   float* sc = reinterpret_cast<float*>(smem4);             // [R][n_kb]
   // [kWaves][256] 64-bit weight histograms, 8-byte aligned after the scores
   uint64_t* hist = reinterpret_cast<uint64_t*>(sc + ((R * n_kb + 1) & ~int64_t(1)));
 
-  const int64_t bh = blockIdx.x / n_groups;
-  const int64_t row0 = (blockIdx.x - bh * n_groups) * R;
+  int64_t bh, group;
+  work_item(n_groups, BH, deal, bh, group);
+  if (bh >= BH) return;
+  const int64_t row0 = group * R;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
@@ -348,17 +371,28 @@ __global__ __launch_bounds__(kThreads) void predict_cdf_kernel(
   }
 }
 
+// Heads are dealt whole to XCDs when that leaves the XCDs evenly loaded (at
+// most one head in eight more on the busiest XCD than an even split).
+int deal_heads(int64_t BH) {
+  const int64_t per = (BH + kNumXcd - 1) / kNumXcd;
+  return BH >= kNumXcd && (per * kNumXcd - BH) * 8 <= BH;
+}
+int64_t grid_size(int64_t BH, int64_t n_groups, int deal) {
+  return deal ? kNumXcd * ((BH + kNumXcd - 1) / kNumXcd) * n_groups : BH * n_groups;
+}
+
 template <int D, int R>
 hipError_t launch_predict_t(const float* qbar, const float* kbar, int64_t BH, int64_t N, int64_t n_qb,
                             int64_t n_kb, int64_t k, double topk, int causal, float scale,
                             uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt, hipStream_t stream) {
   const int64_t n_groups = (n_qb + R - 1) / R;
   const size_t lds = sizeof(float) * R * n_kb + sizeof(uint32_t) * kWaves * 256;
+  const int deal = deal_heads(BH);
   void* args[] = {(void*)&qbar, (void*)&kbar, (void*)&N, (void*)&n_qb, (void*)&n_kb,
-                  (void*)&n_groups, (void*)&k, (void*)&topk, (void*)&causal, (void*)&scale,
-                  (void*)&mask, (void*)&kv_idx, (void*)&kv_cnt};
+                  (void*)&n_groups, (void*)&BH, (void*)&deal, (void*)&k, (void*)&topk, (void*)&causal,
+                  (void*)&scale, (void*)&mask, (void*)&kv_idx, (void*)&kv_cnt};
   return hipLaunchKernel(reinterpret_cast<const void*>(&predict_kernel<D, R>),
-                         dim3(static_cast<uint32_t>(BH * n_groups)), dim3(kThreads), args, lds,
+                         dim3(static_cast<uint32_t>(grid_size(BH, n_groups, deal))), dim3(kThreads), args, lds,
                          stream);
 }
 
@@ -381,11 +415,12 @@ hipError_t launch_cdf_t(const float* qbar, const float* kbar, int64_t BH, int64_
                         int32_t* kv_idx, int32_t* kv_cnt, hipStream_t stream) {
   const int64_t n_groups = (n_qb + R - 1) / R;
   const size_t lds = sizeof(float) * ((R * n_kb + 1) & ~int64_t(1)) + sizeof(uint64_t) * kWaves * 256;
+  const int deal = deal_heads(BH);
   void* args[] = {(void*)&qbar, (void*)&kbar, (void*)&N, (void*)&n_qb, (void*)&n_kb,
-                  (void*)&n_groups, (void*)&tau, (void*)&causal, (void*)&scale,
+                  (void*)&n_groups, (void*)&BH, (void*)&deal, (void*)&tau, (void*)&causal, (void*)&scale,
                   (void*)&mask, (void*)&kv_idx, (void*)&kv_cnt};
   return hipLaunchKernel(reinterpret_cast<const void*>(&predict_cdf_kernel<D, R>),
-                         dim3(static_cast<uint32_t>(BH * n_groups)), dim3(kThreads), args, lds,
+                         dim3(static_cast<uint32_t>(grid_size(BH, n_groups, deal))), dim3(kThreads), args, lds,
                          stream);
 }
 
