@@ -33,7 +33,10 @@
 // Memory
 //   Q rows stay in registers for the whole walk. K and V tiles go global -> LDS
 //   with buffer_load_dwordx4 ... lds (no data registers, no LDS write
-//   instructions), double buffered with one barrier per tile. The loads of
+//   instructions), double buffered with one barrier per tile. The loads are
+//   issued as inline assembly, invisible to the compiler's wait insertion: the
+//   only wait for them is the explicit vmcnt(0) before the barrier that
+//   publishes a stage, so reads of the current stage never wait on them. The loads of
 //   tile t+1 are interleaved one by one with the QK MFMAs of tile t: issued as
 //   a burst right after the barrier, the loads of all eight wavefronts of a CU
 //   fill the vector-memory queue and stall instruction issue for hundreds of
@@ -92,7 +95,7 @@ struct Params {
 // Key block visited at step tt. An id outside [0, n_kb) maps to a block past
 // the end of the sequence whose keys are all masked, so a corrupt list entry
 // contributes nothing instead of reading out of bounds.
-__device__ __forceinline__ int64_t sanitize_id(int64_t j, int64_t n_kb) {
+__device__ __forceinline__ int32_t sanitize_id(int32_t j, int32_t n_kb) {
   return (j >= 0 && j < n_kb) ? j : n_kb;
 }
 __device__ __forceinline__ int64_t block_id(const int32_t* list, int tt, int64_t n_kb) {
@@ -110,6 +113,19 @@ __device__ __forceinline__ float sum_with_partner(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// One LDS-DMA load: 16 bytes per lane from buffer `rs` at byte offset `voff`
+// into LDS at byte address `lds` + 16 * lane. Issued as inline assembly (no
+// result registers; m0 set in the same statement), so the compiler does not
+// see an LDS write: the one wait for these loads is the explicit vmcnt(0)
+// before the barrier that publishes a stage.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void dma16(i32x4 rs, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rs), "s"(lds)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ uint4 load16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
@@ -117,12 +133,8 @@ __device__ __forceinline__ uint4 load16(const uint16_t* p) {
 template <int D, bool kCausal>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   using C = Cfg<D>;
-  // Four separate LDS objects (not one array) so that waits for the loads
-  // filling one buffer are not imposed on reads of another.
-  __shared__ __attribute__((aligned(1024))) char lds_k0[C::kTile];
-  __shared__ __attribute__((aligned(1024))) char lds_k1[C::kTile];
-  __shared__ __attribute__((aligned(1024))) char lds_v0[C::kTile];
-  __shared__ __attribute__((aligned(1024))) char lds_v1[C::kTile];
+  // Tile buffers: K stage 0, K stage 1, V stage 0, V stage 1.
+  __shared__ __attribute__((aligned(1024))) char smem[4 * C::kTile];
 
   // Workgroup -> (head, query block). Consecutive workgroup ids go to
   // consecutive XCDs. Non-causal lists are about equally long: XCD x owns query
@@ -168,7 +180,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   } else {
     cnt = static_cast<int>(p.n_kb);
   }
-  auto raw_id = [&](int i) -> int64_t { return (i < cnt) ? (list ? list[i] : i) : 0; };
+  auto raw_id = [&](int i) -> int32_t { return (i < cnt) ? (list ? list[i] : i) : 0; };
+  const int32_t n_kb32 = static_cast<int32_t>(p.n_kb);
+  const int32_t n32 = static_cast<int32_t>(p.N);
 
   // Q^T operands: lane (n, g) holds query row qrow, columns 16s + 8g .. +7.
   const int64_t qrow = qb * kQBlock + wave * 32 + n;
@@ -208,36 +222,46 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   }
   // Tile j of an operand starts j * tile_bytes past its head; its bound is the
   // whole tile, the rows left at the sequence end, or nothing (j past the end).
-  const int64_t n_full = p.N / kKBlock;
+  const int32_t n_full = static_cast<int32_t>(p.N / kKBlock);
   const uint32_t k_tile = static_cast<uint32_t>(kKBlock * p.ks.n * 2);
   const uint32_t v_tile = static_cast<uint32_t>(kKBlock * p.vs.n * 2);
   const uint32_t k_tail = static_cast<uint32_t>((p.N - n_full * kKBlock) * p.ks.n * 2);
   const uint32_t v_tail = static_cast<uint32_t>((p.N - n_full * kKBlock) * p.vs.n * 2);
-  auto tile_rsrc = [&](const uint16_t* base, int64_t j, uint32_t tile_bytes, uint32_t tail_bytes) {
+  auto tile_rsrc = [&](const uint16_t* base, int32_t j, uint32_t tile_bytes, uint32_t tail_bytes) {
     const uint32_t bound = geom::tile_bound(j, n_full, tile_bytes, tail_bytes);
-    const char* ptr = reinterpret_cast<const char*>(base) +
-                      static_cast<uint64_t>(static_cast<uint32_t>(j)) * tile_bytes;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(ptr), static_cast<short>(0),
-                                             static_cast<int>(bound), kBufferFlags);
+    const uint64_t ptr = reinterpret_cast<uint64_t>(base) + static_cast<uint64_t>(static_cast<uint32_t>(j)) * tile_bytes;
+    i32x4 r;
+    r[0] = static_cast<int>(static_cast<uint32_t>(ptr));
+    r[1] = static_cast<int>(static_cast<uint32_t>(ptr >> 32) & 0xffffu);
+    r[2] = static_cast<int>(bound);
+    r[3] = kBufferFlags;
+    return r;
   };
-  auto issue_one = [&](__amdgpu_buffer_rsrc_t rs, uint32_t off, char* buf, int e) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + geom::load_lds<D>(wave_s, e)),
-                                             16, static_cast<int>(off), 0, 0, 0);
+  // LDS byte address of this wavefront's part of the tile buffers (load_lds is
+  // linear: load_lds(wave, e) = load_lds(wave, 0) + load_lds(0, e)). It is made
+  // opaque once per step, so the compiler forms each load's address with one
+  // scalar add instead of keeping sixteen addresses live (and spilled to
+  // vector lanes).
+  typedef __attribute__((address_space(3))) char lds_char;
+  const uint32_t lds_wave = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char*)smem)) +
+                            static_cast<uint32_t>(geom::load_lds<D>(wave_s, 0));
+  auto issue_one = [&](i32x4 rs, uint32_t off, uint32_t lds_base, int buf, int e) {
+    dma16(rs, off, lds_base + buf * C::kTile + geom::load_lds<D>(0, e));
   };
   // Pins a load between the MFMAs around it: VALU, SALU, transcendental and
   // LDS-read instructions may still move across, MFMAs and memory loads may not.
-  auto pinned_issue = [&](__amdgpu_buffer_rsrc_t rs, uint32_t off, char* buf, int e) {
+  auto pinned_issue = [&](i32x4 rs, uint32_t off, uint32_t lds_base, int buf, int e) {
     __builtin_amdgcn_sched_barrier(kSchedKeepLoads);
-    issue_one(rs, off, buf, e);
+    issue_one(rs, off, lds_base, buf, e);
     __builtin_amdgcn_sched_barrier(kSchedKeepLoads);
   };
-  auto issue = [&](int64_t j, char* kbuf, char* vbuf) {
-    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kh, j, k_tile, k_tail);
-    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vh, j, v_tile, v_tail);
+  auto issue = [&](int32_t j, int kbuf, int vbuf) {
+    const i32x4 kr = tile_rsrc(kh, j, k_tile, k_tail);
+    const i32x4 vr = tile_rsrc(vh, j, v_tile, v_tail);
 #pragma unroll
     for (int e = 0; e < C::kInstPerWave; ++e) {
-      issue_one(kr, ld_koff[e], kbuf, e);
-      issue_one(vr, ld_voff[e], vbuf, e);
+      issue_one(kr, ld_koff[e], lds_wave, kbuf, e);
+      issue_one(vr, ld_voff[e], lds_wave, vbuf, e);
     }
   };
 
@@ -258,14 +282,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   // Keys past N in a ragged (or invalid) block take no weight, and with causal
   // masking neither do keys after this lane's query row. Only tiles at the
   // sequence end or across the block's diagonal need the per-key test.
-  auto mask_keys = [&](int64_t j, f32x16& s0, f32x16& s1) {
-    const int64_t k0 = j * kKBlock;
-    if (k0 + kKBlock > p.N || (kCausal && k0 + kKBlock - 1 > qb * kQBlock)) {
+  auto mask_keys = [&](int32_t j, f32x16& s0, f32x16& s1) {
+    const int32_t k0 = j * kKBlock;
+    if (k0 + kKBlock > n32 || (kCausal && k0 + kKBlock - 1 > static_cast<int32_t>(qb) * kQBlock)) {
       // keys k0 + lim and later are masked; register i of this lane holds key
       // 8g + i (i < 8) or 8g + 16 + (i - 8)
-      int64_t lim64 = p.N - k0;
-      if (kCausal && qrow - k0 + 1 < lim64) lim64 = qrow - k0 + 1;
-      const int lim = static_cast<int>(lim64 < 0 ? 0 : (lim64 > kKBlock ? kKBlock : lim64)) - 8 * g;
+      int32_t lim32 = n32 - k0;
+      if (kCausal && static_cast<int32_t>(qrow) - k0 + 1 < lim32) lim32 = static_cast<int32_t>(qrow) - k0 + 1;
+      const int lim = (lim32 < 0 ? 0 : (lim32 > kKBlock ? kKBlock : lim32)) - 8 * g;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int kl = (i < 8) ? i : 16 + (i - 8);
@@ -356,25 +380,28 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   if (cnt > 0) {
     // Double buffering: step t computes tile t from buffers t%2 while the
     // loads of tile t+1 fill the other pair.
-    int64_t j0 = sanitize_id(raw_id(0), p.n_kb);
-    int64_t j1 = sanitize_id(raw_id(1), p.n_kb);
-    issue(j0, lds_k0, lds_v0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    int32_t j0 = sanitize_id(raw_id(0), n_kb32);
+    int32_t j1 = sanitize_id(raw_id(1), n_kb32);
+    issue(j0, 0, 2);
+    // vmcnt(0) as a builtin, so that the compiler counts the Q loads as done too
+    __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
 
     // The next tile's loads are spread through this tile's QK MFMAs, one load
     // per k-step.
     auto step = [&](auto parity, int tt) {
       constexpr int P = decltype(parity)::value;
-      char* k_cur = P ? lds_k1 : lds_k0;
-      char* v_cur = P ? lds_v1 : lds_v0;
-      char* k_fill = P ? lds_k0 : lds_k1;
-      char* v_fill = P ? lds_v0 : lds_v1;
+      const char* k_cur = smem + (P ? 1 : 0) * C::kTile;
+      const char* v_cur = smem + (P ? 3 : 2) * C::kTile;
+      constexpr int k_fill = P ? 0 : 1;
+      constexpr int v_fill = P ? 2 : 3;
+      uint32_t lds_base = lds_wave;
+      asm volatile("" : "+s"(lds_base));
       const bool more = tt + 1 < cnt;
       // past the last tile the resources hold no bytes: the loads only write
       // zeros into the buffer that was just released
-      const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kh, more ? j1 : p.n_kb, k_tile, k_tail);
-      const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vh, more ? j1 : p.n_kb, v_tile, v_tail);
+      const i32x4 kr = tile_rsrc(kh, more ? j1 : n_kb32, k_tile, k_tail);
+      const i32x4 vr = tile_rsrc(vh, more ? j1 : n_kb32, v_tile, v_tail);
       const int32_t raw2 = static_cast<int32_t>(raw_id(tt + 2));
       f32x16 sa, sb;
       // The QK phase (MFMAs and the tile loads) runs at raised wavefront
@@ -388,8 +415,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) {
           if ((i * C::kSteps) / kLoads == st) {
-            if (i < C::kInstPerWave) pinned_issue(kr, ld_koff[i], k_fill, i);
-            else pinned_issue(vr, ld_voff[i - C::kInstPerWave], v_fill, i - C::kInstPerWave);
+            if (i < C::kInstPerWave) pinned_issue(kr, ld_koff[i], lds_base, k_fill, i);
+            else pinned_issue(vr, ld_voff[i - C::kInstPerWave], lds_base, v_fill, i - C::kInstPerWave);
           }
         }
       });
@@ -399,7 +426,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
       weights(sa, sb, pb);
       pv(v_cur, pb);
       j0 = j1;
-      j1 = sanitize_id(raw2, p.n_kb);
+      j1 = sanitize_id(raw2, n_kb32);
       if (more) {
         // This wavefront's loads of tile t+1 have landed; the barrier makes
         // every wavefront's loads visible and frees the buffers just read.

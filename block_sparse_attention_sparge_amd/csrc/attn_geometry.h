@@ -67,7 +67,7 @@ __host__ __device__ inline uint32_t load_offset(int wave, int e, int lane, int64
 // Byte bound of tile j's buffer resource: the whole tile for the n_full full
 // tiles, the rows left at the sequence end for tile n_full, nothing past it.
 // Loads at offsets >= the bound read zeros and touch no memory.
-__host__ __device__ inline uint32_t tile_bound(int64_t j, int64_t n_full, uint32_t tile_bytes,
+__host__ __device__ inline uint32_t tile_bound(int32_t j, int32_t n_full, uint32_t tile_bytes,
                                                uint32_t tail_bytes) {
   return j < n_full ? tile_bytes : (j == n_full ? tail_bytes : 0u);
 }
