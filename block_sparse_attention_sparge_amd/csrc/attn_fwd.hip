@@ -199,6 +199,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[cc][i] = 0.f;
   float m = -INFINITY;
+  float mref = 0.f;        // m, or 0 while m is unset (m only changes on the exact path)
+  bool all_ref = false;    // wavefront-uniform: every lane has a reference m
   float l = 0.f;
 
   // ---- per-lane LDS geometry (constant over the walk; see attn_geometry.h)
@@ -336,9 +338,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   auto weights = [&](const f32x16& s0, const f32x16& s1, bf16x8 (&pb)[4]) {
     // m stays -inf only while every key seen so far was masked (invalid ids);
     // a reference of 0 then gives zero weights instead of NaN.
-    float mref = (m == -INFINITY) ? 0.f : m;
     float lt = probs(s0, s1, mref, pb);
-    if (__builtin_amdgcn_ballot_w64(m == -INFINITY || !(lt <= kSumLimit))) {
+    if (!all_ref || __builtin_amdgcn_ballot_w64(!(lt <= kSumLimit))) {
       float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
@@ -353,6 +354,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
         for (int i = 0; i < 16; ++i) o[cc][i] *= alpha;
       m = m_new;
       mref = (m == -INFINITY) ? 0.f : m;
+      all_ref = __builtin_amdgcn_ballot_w64(m == -INFINITY) == 0;
       lt = probs(s0, s1, mref, pb);
     }
     l += lt;
