@@ -20,6 +20,8 @@ namespace {
 constexpr int64_t kMaxDim = int64_t(1) << 40;   // guards the size arithmetic below against overflow
 constexpr size_t kAlign = 256;
 constexpr int64_t kMaxRowStride = int64_t(1) << 24;   // elements between consecutive tokens
+// the attention kernel computes key positions (block * 64 + 64) and query rows in 32 bits
+constexpr int64_t kMaxAttnN = (int64_t(1) << 31) - 128;
 
 bool valid_d(int64_t D) { return D == 64 || D == 128; }
 
@@ -116,6 +118,7 @@ int check_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t
                const int64_t* vs, const int64_t* os) {
   if (!q || !k || !v || !out) return SPARGE_ERR_NULL;
   if (int rc = check_shape(B, H, N, D)) return rc;
+  if (N > kMaxAttnN) return SPARGE_ERR_SHAPE;
   for (const int64_t* s : {qs, ks, vs, os})
     if (int rc = check_strides(s)) return rc;
   // the attention kernel addresses the rows of one 64-key tile with 32-bit byte offsets

@@ -31,7 +31,9 @@
  *    Q, K and V at most 2^24 elements, and that of K and V at least D, so
  *    that their rows do not overlap) and every base
  *    address 16-byte aligned, so that a row of 8 bf16 is one aligned load.
- *  - D (head dimension) must be 64 or 128. N >= 1, B >= 1, H >= 1.
+ *  - D (head dimension) must be 64 or 128. N >= 1, B >= 1, H >= 1; the calls
+ *    that run attention also need N <= 2^31 - 128 (the kernel's key and row
+ *    arithmetic is 32-bit; four such tensors would not fit in HBM anyway).
  *  - N_QB = ceil(N/128) query blocks and N_KB = ceil(N/64) key blocks.
  *  - scale <= 0 means the default 1/sqrt(D).
  *  - is_causal is 0 (non-causal) or 1 (causal, see above); other values are

@@ -104,6 +104,7 @@ def test_attention_argument_errors(lib, fn):
     assert attn_call(lib, fn, D=96, mask=mask) == SHAPE
     assert attn_call(lib, fn, N=0, mask=mask) == SHAPE
     assert attn_call(lib, fn, B=0, mask=mask) == SHAPE
+    assert attn_call(lib, fn, N=(1 << 31) - 127, mask=mask) == SHAPE                 # 32-bit key arithmetic
     assert attn_call(lib, fn, qs=S(2 * 256 * 64, 256 * 64, 60), mask=mask) == STRIDE   # not a multiple of 8
     assert attn_call(lib, fn, ks=S(-8, 256 * 64, 64), mask=mask) == STRIDE
     assert attn_call(lib, fn, q=A + 8, mask=mask) == STRIDE                          # misaligned
