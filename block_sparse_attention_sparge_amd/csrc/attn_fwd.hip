@@ -36,7 +36,11 @@
 //   instructions), double buffered with one barrier per tile. The loads are
 //   issued as inline assembly, invisible to the compiler's wait insertion: the
 //   only wait for them is the explicit vmcnt(0) before the barrier that
-//   publishes a stage, so reads of the current stage never wait on them. The loads of
+//   publishes a stage, so reads of the current stage never wait on them.
+//   MFMA operands are read from LDS ahead of their use (K two k-steps ahead,
+//   V^T two MFMAs ahead), an order imposed on the scheduler with
+//   sched_group_barrier: left to itself it reads each operand right before
+//   its MFMA and the MFMA waits out the LDS latency. The loads of
 //   tile t+1 are interleaved one by one with the QK MFMAs of tile t: issued as
 //   a burst right after the barrier, the loads of all eight wavefronts of a CU
 //   fill the vector-memory queue and stall instruction issue for hundreds of
@@ -69,8 +73,9 @@ constexpr int kSumLog2 = 20;            // per-lane weight sum that triggers a n
 constexpr float kSumLimit = static_cast<float>(1 << kSumLog2);
 // Word 3 of a raw (untyped) buffer resource on gfx9-family parts.
 constexpr int kBufferFlags = 0x00020000;
-// sched_barrier mask: VALU (0x2), SALU (0x4), LDS reads (0x100), transcendental (0x400).
-constexpr int kSchedKeepLoads = 0x0506;
+// sched_group_barrier instruction classes: MFMA (0x8), LDS reads (0x100).
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedLdsRead = 0x100;
 
 template <int D>
 struct Cfg : geom::Tile<D> {
@@ -250,13 +255,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   auto issue_one = [&](i32x4 rs, uint32_t off, uint32_t lds_base, int buf, int e) {
     dma16(rs, off, lds_base + buf * C::kTile + geom::load_lds<D>(0, e));
   };
-  // Pins a load between the MFMAs around it: VALU, SALU, transcendental and
-  // LDS-read instructions may still move across, MFMAs and memory loads may not.
-  auto pinned_issue = [&](i32x4 rs, uint32_t off, uint32_t lds_base, int buf, int e) {
-    __builtin_amdgcn_sched_barrier(kSchedKeepLoads);
-    issue_one(rs, off, lds_base, buf, e);
-    __builtin_amdgcn_sched_barrier(kSchedKeepLoads);
-  };
   auto issue = [&](int32_t j, int kbuf, int vbuf) {
     const i32x4 kr = tile_rsrc(kh, j, k_tile, k_tail);
     const i32x4 vr = tile_rsrc(vh, j, v_tile, v_tail);
@@ -271,13 +269,29 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   auto qk = [&](const char* kb, f32x16& s0, f32x16& s1, auto hook) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) { s0[i] = 0.f; s1[i] = 0.f; }
+    // K fragments two k-steps ahead of their MFMAs
+    bf16x8 ka[2][2];
+    auto rd = [&](int s, bf16x8 (&d)[2]) {
+      d[0] = *reinterpret_cast<const bf16x8*>(kb + koff[s]);
+      d[1] = *reinterpret_cast<const bf16x8*>(kb + koff[s] + 32 * C::kRowBytes);
+    };
+    rd(0, ka[0]);
+    if (C::kSteps > 1) rd(1, ka[1]);
 #pragma unroll
     for (int s = 0; s < C::kSteps; ++s) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kb + koff[s]);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kb + koff[s] + 32 * C::kRowBytes);
+      const bf16x8 a0 = ka[s & 1][0], a1 = ka[s & 1][1];
+      if (s + 2 < C::kSteps) rd(s + 2, ka[s & 1]);
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[s], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[s], s1, 0, 0, 0);
       hook(s);
+    }
+    // issue order: the first two k-steps' K reads, then per k-step its two
+    // MFMAs followed by the reads of the k-step two ahead
+    __builtin_amdgcn_sched_group_barrier(kSchedLdsRead, 4, 0);
+#pragma unroll
+    for (int s = 0; s < C::kSteps; ++s) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+      if (s + 2 < C::kSteps) __builtin_amdgcn_sched_group_barrier(kSchedLdsRead, 2, 0);
     }
   };
 
@@ -377,6 +391,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
         o[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[u], o[cc], 0, 0, 0);
       }
     }
+    // issue order: the first two MFMAs' V^T reads, then each MFMA followed by
+    // the reads of the MFMA two ahead
+    __builtin_amdgcn_sched_group_barrier(kSchedLdsRead, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * C::kDChunks; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      if (i + 2 < 4 * C::kDChunks) __builtin_amdgcn_sched_group_barrier(kSchedLdsRead, 2, 0);
+    }
   };
 
   if (cnt > 0) {
@@ -404,7 +426,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
       // zeros into the buffer that was just released
       const i32x4 kr = tile_rsrc(kh, more ? j1 : n_kb32, k_tile, k_tail);
       const i32x4 vr = tile_rsrc(vh, more ? j1 : n_kb32, v_tile, v_tail);
-      const int32_t raw2 = static_cast<int32_t>(raw_id(tt + 2));
       f32x16 sa, sb;
       // The QK phase (MFMAs and the tile loads) runs at raised wavefront
       // priority, so the SIMD's other wavefront fills in with its softmax.
@@ -417,8 +438,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) {
           if ((i * C::kSteps) / kLoads == st) {
-            if (i < C::kInstPerWave) pinned_issue(kr, ld_koff[i], lds_base, k_fill, i);
-            else pinned_issue(vr, ld_voff[i - C::kInstPerWave], lds_base, v_fill, i - C::kInstPerWave);
+            if (i < C::kInstPerWave) issue_one(kr, ld_koff[i], lds_base, k_fill, i);
+            else issue_one(vr, ld_voff[i - C::kInstPerWave], lds_base, v_fill, i - C::kInstPerWave);
           }
         }
       });
@@ -427,6 +448,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
       bf16x8 pb[4];
       weights(sa, sb, pb);
       pv(v_cur, pb);
+      // the id two tiles ahead is read here, where the step-end wait covers
+      // its scalar load, not at the next QK's first operand wait
+      const int32_t raw2 = static_cast<int32_t>(raw_id(tt + 2));
       j0 = j1;
       j1 = sanitize_id(raw2, n_kb32);
       if (more) {
