@@ -119,16 +119,14 @@ __device__ __forceinline__ float sum_with_partner(float x) {
 }
 
 // One LDS-DMA load: 16 bytes per lane from buffer `rs` at byte offset `voff`
-// into LDS at byte address `lds` + 16 * lane. Issued as inline assembly (no
-// result registers; m0 set in the same statement), so the compiler does not
-// see an LDS write: the one wait for these loads is the explicit vmcnt(0)
-// before the barrier that publishes a stage.
+// into LDS at byte address `lds` + 16 * lane (m0 holds the LDS address; it is
+// an input operand, so the compiler sets it and knows its value). Issued as
+// inline assembly with no result registers, so the compiler does not see an
+// LDS write: the one wait for these loads is the explicit vmcnt(0) before the
+// barrier that publishes a stage.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void dma16(i32x4 rs, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(voff), "s"(rs), "s"(lds)
-               : "memory", "m0");
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rs), "{m0}"(lds) : "memory");
 }
 
 __device__ __forceinline__ uint4 load16(const uint16_t* p) {
