@@ -442,13 +442,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
         }
       });
       __builtin_amdgcn_s_setprio(0);
+      // The block id two tiles ahead is read here: the softmax has no LDS
+      // reads for its scalar load to hold up (scalar and LDS loads share a
+      // counter, and an outstanding scalar load forces full waits), and it has
+      // landed by the time PV waits for its first operands.
+      const int32_t raw2 = static_cast<int32_t>(raw_id(tt + 2));
       mask_keys(j0, sa, sb);
       bf16x8 pb[4];
       weights(sa, sb, pb);
       pv(v_cur, pb);
-      // the id two tiles ahead is read here, where the step-end wait covers
-      // its scalar load, not at the next QK's first operand wait
-      const int32_t raw2 = static_cast<int32_t>(raw_id(tt + 2));
       j0 = j1;
       j1 = sanitize_id(raw2, n_kb32);
       if (more) {
