@@ -133,7 +133,7 @@ __device__ __forceinline__ uint4 load16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
-template <int D, bool kCausal>
+template <int D, bool kCausal, bool kSameKV>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   using C = Cfg<D>;
   // Tile buffers: K stage 0, K stage 1, V stage 0, V stage 1.
@@ -405,6 +405,36 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
     int32_t j0 = sanitize_id(raw_id(0), n_kb32);
     int32_t j1 = sanitize_id(raw_id(1), n_kb32);
     issue(j0, 0, 2);
+    // Buffer resources of the loads a step issues (tile t+1 in step t), set
+    // at the end of the previous step, where the wavefront goes on to wait at
+    // the barrier: the scalar work is off the path into the next QK. Past the
+    // last tile they hold no bytes, so those loads only write zeros into the
+    // buffers just released. With equal K and V token strides one product
+    // and one bound serve both.
+    i32x4 kr, vr;
+    kr[3] = kBufferFlags;
+    vr[3] = kBufferFlags;
+    const uint64_t kbase = reinterpret_cast<uint64_t>(kh), vbase = reinterpret_cast<uint64_t>(vh);
+    auto set_next = [&](int32_t j) {
+      const uint64_t kp = kbase + static_cast<uint64_t>(static_cast<uint32_t>(j)) * k_tile;
+      const uint32_t kb = geom::tile_bound(j, n_full, k_tile, k_tail);
+      kr[0] = static_cast<int>(static_cast<uint32_t>(kp));
+      kr[1] = static_cast<int>(static_cast<uint32_t>(kp >> 32) & 0xffffu);
+      kr[2] = static_cast<int>(kb);
+      uint64_t vp;
+      uint32_t vb;
+      if constexpr (kSameKV) {
+        vp = vbase + (kp - kbase);
+        vb = kb;
+      } else {
+        vp = vbase + static_cast<uint64_t>(static_cast<uint32_t>(j)) * v_tile;
+        vb = geom::tile_bound(j, n_full, v_tile, v_tail);
+      }
+      vr[0] = static_cast<int>(static_cast<uint32_t>(vp));
+      vr[1] = static_cast<int>(static_cast<uint32_t>(vp >> 32) & 0xffffu);
+      vr[2] = static_cast<int>(vb);
+    };
+    set_next(cnt > 1 ? j1 : n_kb32);
     // vmcnt(0) as a builtin, so that the compiler counts the Q loads as done too
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
@@ -420,11 +450,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
       uint32_t lds_base = lds_wave;
       asm volatile("" : "+s"(lds_base));
       const bool more = tt + 1 < cnt;
-      // past the last tile the resources hold no bytes: the loads only write
-      // zeros into the buffer that was just released
-      const i32x4 kr = tile_rsrc(kh, more ? j1 : n_kb32, k_tile, k_tail);
-      const i32x4 vr = tile_rsrc(vh, more ? j1 : n_kb32, v_tile, v_tail);
-      f32x16 sa, sb;
+        f32x16 sa, sb;
       // The QK phase (MFMAs and the tile loads) runs at raised wavefront
       // priority, so the SIMD's other wavefront fills in with its softmax.
       __builtin_amdgcn_s_setprio(2);
@@ -454,6 +480,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
       j0 = j1;
       j1 = sanitize_id(raw2, n_kb32);
       if (more) {
+        set_next(tt + 2 < cnt ? j1 : n_kb32);
         // This wavefront's loads of tile t+1 have landed; the barrier makes
         // every wavefront's loads visible and frees the buffers just read.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -498,8 +525,11 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   p.c = a.scale * kLog2e;
   const int64_t grid = a.B * a.H * kNumXcd * p.per_xcd;
   void* args[] = {(void*)&p};
-  const void* fn = a.causal ? reinterpret_cast<const void*>(&attn_fwd_kernel<D, true>)
-                           : reinterpret_cast<const void*>(&attn_fwd_kernel<D, false>);
+  const bool same = a.ks.n == a.vs.n;
+  const void* fn = a.causal ? (same ? reinterpret_cast<const void*>(&attn_fwd_kernel<D, true, true>)
+                                    : reinterpret_cast<const void*>(&attn_fwd_kernel<D, true, false>))
+                            : (same ? reinterpret_cast<const void*>(&attn_fwd_kernel<D, false, true>)
+                                    : reinterpret_cast<const void*>(&attn_fwd_kernel<D, false, false>));
   return hipLaunchKernel(fn,
                          dim3(static_cast<uint32_t>(grid)), dim3(256), args, 0, stream);
 }
