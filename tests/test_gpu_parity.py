@@ -191,6 +191,26 @@ def test_strided_layouts_and_scale(gpu_lib):
 
 
 @pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_kv_strides_differ(gpu_lib, D, causal):
+    """K and V with different token strides (K contiguous, V stored (B, N, H, D))
+    take the kernel's separate K and V tile bounds; ragged N, so the tail tile
+    is bounded differently for each."""
+    B, H, N = 2, 3, 700
+    q, k, v = rand_qkv(B, H, N, D, seed=23)
+    dq, dk, dv = _dev(q, k, v)
+    tv = dv.transpose(1, 2).contiguous().transpose(1, 2)
+    assert tv.stride(2) != dk.stride(2)
+    m = torch.from_numpy(_random_mask(B, H, N, 0.4, seed=5)).cuda()
+    a = sp.block_sparse_attn(dq, dk, dv, mask_id=m, is_causal=causal)
+    b = sp.block_sparse_attn(dq, dk, tv, mask_id=m, is_causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    ref = oracle.masked_attention(F64(q), F64(k), F64(v), m.cpu().numpy(), causal=causal)
+    assert_close(to_host_f64(b), ref, f"K/V strides differ, D={D}, causal={causal}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("pattern", ["growing", "shrinking", "wide"])
 def test_softmax_reference_raised(gpu_lib, D, pattern):
     """Scores that climb far above the running max along the key walk (and the
