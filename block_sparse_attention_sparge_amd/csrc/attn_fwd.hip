@@ -476,6 +476,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
       mask_keys(j0, sa, sb);
       bf16x8 pb[4];
       weights(sa, sb, pb);
+      // the block id's scalar load has long landed; saying so here lets PV's
+      // operand waits count LDS reads only
+      __builtin_amdgcn_s_waitcnt(0xc07f);
       pv(v_cur, pb);
       j0 = j1;
       j1 = sanitize_id(raw2, n_kb32);
