@@ -96,14 +96,11 @@ struct Params {
   float c;             // scale * log2(e)
 };
 
-// Key block visited at step tt. An id outside [0, n_kb) maps to a block past
-// the end of the sequence whose keys are all masked, so a corrupt list entry
-// contributes nothing instead of reading out of bounds.
+// Key block of a list entry. An id outside [0, n_kb) maps to a block past the
+// end of the sequence whose keys are all masked (its tile loads read nothing),
+// so a corrupt list entry contributes nothing instead of reading out of bounds.
 __device__ __forceinline__ int32_t sanitize_id(int32_t j, int32_t n_kb) {
   return (j >= 0 && j < n_kb) ? j : n_kb;
-}
-__device__ __forceinline__ int64_t block_id(const int32_t* list, int tt, int64_t n_kb) {
-  return list ? sanitize_id(list[tt], n_kb) : tt;
 }
 
 // Value of x in the partner lane (lane ^ 32) combined with x: v_permlane32_swap
