@@ -48,10 +48,11 @@
 //   D=128, so two workgroups share a CU) with 16-byte chunks XOR-swizzled per
 //   row: K so that the 16 rows one A-operand read touches hit distinct banks,
 //   V so that the 4 rows of one transpose read do.
-//   Workgroups are numbered so that each of the 8 XCDs (each with its own L2)
-//   walks a contiguous range of query blocks of one head while all XCDs move
-//   through the heads together: one head's K/V stays hot in the last-level
-//   cache and neighbouring query blocks, whose lists overlap, share L2.
+//   Workgroups are numbered so that each round of an XCD's resident
+//   workgroups (each XCD has its own L2) takes consecutive query blocks of one
+//   head while all XCDs move through the heads together: one head's K/V stays
+//   hot in the last-level cache, and the workgroups sharing an L2 start
+//   together on neighbouring query blocks, whose lists overlap.
 #include <type_traits>
 
 #include "attn_geometry.h"
@@ -76,6 +77,11 @@ constexpr int kBufferFlags = 0x00020000;
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedLdsRead = 0x100;
 
+// Resident workgroups per XCD (32 CUs): two per CU at D=128 (64 KB of LDS
+// each), four at D=64.
+template <int D>
+constexpr int64_t kRound = D == 128 ? 64 : 128;
+
 template <int D>
 struct Cfg : geom::Tile<D> {
   static constexpr int kTile = geom::Tile<D>::kBytes;       // one K or V tile in LDS
@@ -91,7 +97,8 @@ struct Params {
   int64_t ld_idx;
   int64_t H, N;
   int64_t n_qb, n_kb;
-  int64_t per_xcd;     // query blocks per XCD slice of a head
+  int64_t per_xcd;     // query blocks per XCD slice of a head (causal order)
+  int64_t n_items;     // B * H * n_qb (head, query block) pairs
   Strides qs, ks, vs, os;
   float c;             // scale * log2(e)
 };
@@ -136,18 +143,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * C::kTile];
 
   // Workgroup -> (head, query block). Consecutive workgroup ids go to
-  // consecutive XCDs. Non-causal lists are about equally long: XCD x owns query
-  // blocks [x*per, (x+1)*per) of every head, so neighbouring blocks, whose
-  // lists overlap, share its L2. Causal lists grow with the block index: each
-  // head's blocks are dispatched longest first and dealt round the XCDs, so
-  // short lists fill in at the end instead of one XCD carrying the long ones.
+  // consecutive XCDs, and an XCD starts its workgroups in id order. Non-causal
+  // lists are equally long, so an XCD's resident workgroups (kRound of them)
+  // run in rounds that start and walk their ascending lists together: the
+  // (head, query block) pairs, in head-major order, are cut into chunks of
+  // kRound and the chunks dealt round the XCDs, so each round on an XCD takes
+  // consecutive query blocks (lists that overlap) of one head, and all XCDs
+  // work on about one head at a time. Causal lists grow with the block index:
+  // each head's blocks are dispatched longest first and dealt round the XCDs,
+  // so short lists fill in at the end instead of one XCD carrying the long ones.
   const int64_t wid = blockIdx.x;
   int64_t bh, qb;
   if constexpr (!kCausal) {
     const int64_t xcd = wid % kNumXcd;
     const int64_t it = wid / kNumXcd;
-    bh = it / p.per_xcd;
-    qb = xcd * p.per_xcd + (it - bh * p.per_xcd);
+    const int64_t item = ((it / kRound<D>) * kNumXcd + xcd) * kRound<D> + (it % kRound<D>);
+    if (item >= p.n_items) return;
+    bh = item / p.n_qb;
+    qb = item - bh * p.n_qb;
   } else {
     const int64_t per_head = kNumXcd * p.per_xcd;
     bh = wid / per_head;
@@ -522,7 +535,10 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   p.per_xcd = (p.n_qb + kNumXcd - 1) / kNumXcd;
   p.qs = a.qs; p.ks = a.ks; p.vs = a.vs; p.os = a.os;
   p.c = a.scale * kLog2e;
-  const int64_t grid = a.B * a.H * kNumXcd * p.per_xcd;
+  p.n_items = a.B * a.H * p.n_qb;
+  const int64_t chunk_round = kRound<D> * kNumXcd;
+  const int64_t grid = a.causal ? a.B * a.H * kNumXcd * p.per_xcd
+                                : (p.n_items + chunk_round - 1) / chunk_round * chunk_round;
   void* args[] = {(void*)&p};
   const bool same = a.ks.n == a.vs.n;
   const void* fn = a.causal ? (same ? reinterpret_cast<const void*>(&attn_fwd_kernel<D, true, true>)
