@@ -97,7 +97,6 @@ struct Params {
   int64_t ld_idx;
   int64_t H, N;
   int64_t n_qb, n_kb;
-  int64_t per_xcd;     // query blocks per XCD slice of a head (causal order)
   int64_t n_items;     // B * H * n_qb (head, query block) pairs
   Strides qs, ks, vs, os;
   float c;             // scale * log2(e)
@@ -143,28 +142,27 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * C::kTile];
 
   // Workgroup -> (head, query block). Consecutive workgroup ids go to
-  // consecutive XCDs, and an XCD starts its workgroups in id order. Non-causal
-  // lists are equally long, so an XCD's resident workgroups (kRound of them)
-  // run in rounds that start and walk their ascending lists together: the
-  // (head, query block) pairs, in head-major order, are cut into chunks of
-  // kRound and the chunks dealt round the XCDs, so each round on an XCD takes
-  // consecutive query blocks (lists that overlap) of one head, and all XCDs
-  // work on about one head at a time. Causal lists grow with the block index:
-  // each head's blocks are dispatched longest first and dealt round the XCDs,
-  // so short lists fill in at the end instead of one XCD carrying the long ones.
+  // consecutive XCDs, and an XCD starts its workgroups in id order, so its
+  // resident workgroups (kRound of them) run in rounds that start, and walk
+  // their ascending lists, together. The (head, query block) pairs, head-major,
+  // are cut into chunks of kRound and the chunks dealt round the XCDs, the
+  // direction reversed every round: each round on an XCD takes consecutive
+  // query blocks (lists that overlap) of one head, all XCDs work on about one
+  // head at a time, and the serpentine deal evens out chunks of unequal work.
+  // Causal lists grow with the block index, so each head's blocks are taken
+  // longest first: the short lists fill in at the end.
   const int64_t wid = blockIdx.x;
   int64_t bh, qb;
-  if constexpr (!kCausal) {
+  {
     const int64_t xcd = wid % kNumXcd;
     const int64_t it = wid / kNumXcd;
-    const int64_t item = ((it / kRound<D>) * kNumXcd + xcd) * kRound<D> + (it % kRound<D>);
+    const int64_t round = it / kRound<D>;
+    const int64_t chunk = round * kNumXcd + ((round & 1) ? kNumXcd - 1 - xcd : xcd);
+    const int64_t item = chunk * kRound<D> + (it - round * kRound<D>);
     if (item >= p.n_items) return;
     bh = item / p.n_qb;
     qb = item - bh * p.n_qb;
-  } else {
-    const int64_t per_head = kNumXcd * p.per_xcd;
-    bh = wid / per_head;
-    qb = p.n_qb - 1 - (wid - bh * per_head);
+    if constexpr (kCausal) qb = p.n_qb - 1 - qb;
   }
   if (qb < 0 || qb >= p.n_qb) return;
   const int64_t b = bh / p.H, h = bh - (bh / p.H) * p.H;
@@ -532,13 +530,11 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   p.H = a.H; p.N = a.N;
   p.n_qb = (a.N + kQBlock - 1) / kQBlock;
   p.n_kb = (a.N + kKBlock - 1) / kKBlock;
-  p.per_xcd = (p.n_qb + kNumXcd - 1) / kNumXcd;
   p.qs = a.qs; p.ks = a.ks; p.vs = a.vs; p.os = a.os;
   p.c = a.scale * kLog2e;
   p.n_items = a.B * a.H * p.n_qb;
   const int64_t chunk_round = kRound<D> * kNumXcd;
-  const int64_t grid = a.causal ? a.B * a.H * kNumXcd * p.per_xcd
-                                : (p.n_items + chunk_round - 1) / chunk_round * chunk_round;
+  const int64_t grid = (p.n_items + chunk_round - 1) / chunk_round * chunk_round;
   void* args[] = {(void*)&p};
   const bool same = a.ks.n == a.vs.n;
   const void* fn = a.causal ? (same ? reinterpret_cast<const void*>(&attn_fwd_kernel<D, true, true>)
