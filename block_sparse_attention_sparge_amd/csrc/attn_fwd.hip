@@ -81,6 +81,7 @@ constexpr int kSchedLdsRead = 0x100;
 // each), four at D=64.
 template <int D>
 constexpr int64_t kRound = D == 128 ? 64 : 128;
+static_assert(geom::kXcdCount == kNumXcd, "one XCD count");
 
 template <int D>
 struct Cfg : geom::Tile<D> {
@@ -141,25 +142,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   // Tile buffers: K stage 0, K stage 1, V stage 0, V stage 1.
   __shared__ __attribute__((aligned(1024))) char smem[4 * C::kTile];
 
-  // Workgroup -> (head, query block). Consecutive workgroup ids go to
-  // consecutive XCDs, and an XCD starts its workgroups in id order, so its
-  // resident workgroups (kRound of them) run in rounds that start, and walk
-  // their ascending lists, together. The (head, query block) pairs, head-major,
-  // are cut into chunks of kRound and the chunks dealt round the XCDs, the
-  // direction reversed every round: each round on an XCD takes consecutive
-  // query blocks (lists that overlap) of one head, all XCDs work on about one
-  // head at a time, and the serpentine deal evens out chunks of unequal work.
-  // Causal lists grow with the block index, so each head's blocks are taken
-  // longest first: the short lists fill in at the end.
-  const int64_t wid = blockIdx.x;
+  // Workgroup -> (head, query block) by geom::work_item: the workgroups
+  // resident on an XCD (kRound of them) run in rounds that start, and walk
+  // their ascending lists, together, and each round takes consecutive query
+  // blocks (lists that overlap) of one head, while all XCDs work on about one
+  // head at a time. Causal lists grow with the block index, so each head's
+  // blocks are taken longest first: the short lists fill in at the end.
   int64_t bh, qb;
   {
-    const int64_t xcd = wid % kNumXcd;
-    const int64_t it = wid / kNumXcd;
-    const int64_t round = it / kRound<D>;
-    const int64_t chunk = round * kNumXcd + ((round & 1) ? kNumXcd - 1 - xcd : xcd);
-    const int64_t item = chunk * kRound<D> + (it - round * kRound<D>);
-    if (item >= p.n_items) return;
+    int64_t item;
+    if (!geom::work_item(blockIdx.x, p.n_items, kRound<D>, item)) return;
     bh = item / p.n_qb;
     qb = item - bh * p.n_qb;
     if constexpr (kCausal) qb = p.n_qb - 1 - qb;
@@ -533,8 +525,7 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   p.qs = a.qs; p.ks = a.ks; p.vs = a.vs; p.os = a.os;
   p.c = a.scale * kLog2e;
   p.n_items = a.B * a.H * p.n_qb;
-  const int64_t chunk_round = kRound<D> * kNumXcd;
-  const int64_t grid = (p.n_items + chunk_round - 1) / chunk_round * chunk_round;
+  const int64_t grid = geom::work_grid(p.n_items, kRound<D>);
   void* args[] = {(void*)&p};
   const bool same = a.ks.n == a.vs.n;
   const void* fn = a.causal ? (same ? reinterpret_cast<const void*>(&attn_fwd_kernel<D, true, true>)

@@ -89,5 +89,28 @@ __host__ __device__ constexpr int v_read(int lane, int cc) {
          8 * (lane & 1);
 }
 
+// Workgroup -> work item of the attention launch. Items are the (head, query
+// block) pairs in head-major order (item = bh * n_qb + qb). Consecutive
+// workgroup ids go to consecutive XCDs, and an XCD starts its workgroups in id
+// order, so the `round` workgroups resident on an XCD at once run in rounds.
+// The items are cut into chunks of `round` and the chunks dealt round the XCDs,
+// 0..7 in even rounds and 7..0 in odd ones: each round on an XCD takes
+// consecutive items, and chunks of unequal work even out. Returns false for
+// the padding workgroups of the last round.
+constexpr int kXcdCount = 8;
+__host__ __device__ inline bool work_item(int64_t wid, int64_t n_items, int64_t round, int64_t& item) {
+  const int64_t xcd = wid % kXcdCount;
+  const int64_t it = wid / kXcdCount;
+  const int64_t r = it / round;
+  const int64_t chunk = r * kXcdCount + ((r & 1) ? kXcdCount - 1 - xcd : xcd);
+  item = chunk * round + (it - r * round);
+  return item < n_items;
+}
+// Workgroups of the launch: whole rounds of every XCD.
+__host__ __device__ inline int64_t work_grid(int64_t n_items, int64_t round) {
+  const int64_t per = round * kXcdCount;
+  return (n_items + per - 1) / per * per;
+}
+
 }  // namespace geom
 }  // namespace sparge

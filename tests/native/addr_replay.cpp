@@ -15,11 +15,18 @@
 //    every V transpose read (every key step, both row quads, every output chunk)
 //    lies inside the tile buffer, and the K reads fetch exactly the logical
 //    chunk (2s + g) of row sigma(n) (+32) that the MFMA operand needs.
+// With --map it checks instead the launch's workgroup -> work-item mapping
+// (geom::work_item, geom::work_grid) for the item counts and round sizes
+// given: every (head, query block) item is taken by exactly one workgroup,
+// padding workgroups take none, each XCD's workgroups come in rounds of
+// consecutive items, and no XCD gets more than one chunk beyond another.
 // Exit status 0 when every check holds; failures are printed.
 //
 // usage: addr_replay [--plant tail|swizzle] D N row_stride [D N row_stride ...]
+//        addr_replay --map [--plant deal] n_items round [n_items round ...]
 // --plant replays a deliberately wrong variant (the tail tile bounded as a full
-// tile, or K loaded with V's swizzle) to show the checks catch it.
+// tile, K loaded with V's swizzle, or the mapping without its in-round offset)
+// to show the checks catch it.
 #include <cstdio>
 #include <cstdlib>
 #include <string>
@@ -30,7 +37,7 @@
 using namespace sparge::geom;
 
 static long failures = 0;
-static int plant = 0;   // 1: tail tile bounded as a full tile; 2: K loads with V's swizzle
+static int plant = 0;   // 1: tail tile bounded as a full tile; 2: K loads with V's swizzle; 3: mapping bug
 #define CHECK(cond, ...)                                  \
   do {                                                    \
     if (!(cond)) {                                        \
@@ -122,7 +129,66 @@ static void replay(int64_t N, int64_t row_stride) {
   }
 }
 
+static void replay_map(int64_t n_items, int64_t round) {
+  const int64_t grid = work_grid(n_items, round);
+  CHECK(grid % (round * kXcdCount) == 0 && grid >= n_items && grid < n_items + round * kXcdCount,
+        "grid %lld for %lld items", (long long)grid, (long long)n_items);
+  std::vector<int> seen(static_cast<size_t>(n_items), 0);
+  std::vector<int64_t> per_xcd(kXcdCount, 0);
+  for (int64_t wid = 0; wid < grid; ++wid) {
+    int64_t item;
+    bool ok = work_item(wid, n_items, round, item);
+    if (plant == 3) {   // the in-round offset dropped
+      const int64_t it = wid / kXcdCount, r = it / round, x = wid % kXcdCount;
+      item = (r * kXcdCount + ((r & 1) ? kXcdCount - 1 - x : x)) * round;
+      ok = item < n_items;
+    }
+    if (!ok) {
+      CHECK(item >= n_items, "workgroup %lld refused item %lld < %lld", (long long)wid, (long long)item,
+            (long long)n_items);
+      continue;
+    }
+    CHECK(item >= 0 && item < n_items, "workgroup %lld took item %lld", (long long)wid, (long long)item);
+    if (item < 0 || item >= n_items) continue;
+    ++seen[static_cast<size_t>(item)];
+    ++per_xcd[static_cast<size_t>(wid % kXcdCount)];
+    // the workgroups of one round on an XCD take consecutive items
+    const int64_t it = wid / kXcdCount;
+    if (it % round != 0) {
+      int64_t first;
+      work_item(wid - (it % round) * kXcdCount, n_items, round, first);
+      CHECK(item - first == it % round, "round of XCD %lld not consecutive at workgroup %lld",
+            (long long)(wid % kXcdCount), (long long)wid);
+    }
+  }
+  for (int64_t i = 0; i < n_items; ++i)
+    CHECK(seen[static_cast<size_t>(i)] == 1, "item %lld taken %d times", (long long)i, seen[static_cast<size_t>(i)]);
+  int64_t lo = per_xcd[0], hi = per_xcd[0];
+  for (int64_t c : per_xcd) { lo = c < lo ? c : lo; hi = c > hi ? c : hi; }
+  CHECK(hi - lo <= round, "XCD loads %lld..%lld differ by more than a chunk", (long long)lo, (long long)hi);
+}
+
 int main(int argc, char** argv) {
+  if (argc > 1 && std::string(argv[1]) == "--map") {
+    argv += 1;
+    argc -= 1;
+    if (argc > 2 && std::string(argv[1]) == "--plant" && std::string(argv[2]) == "deal") {
+      plant = 3;
+      argv += 2;
+      argc -= 2;
+    }
+    if (argc < 3 || (argc - 1) % 2 != 0) {
+      std::fprintf(stderr, "usage: addr_replay --map n_items round [...]\n");
+      return 2;
+    }
+    int cases = 0;
+    for (int i = 1; i + 1 < argc; i += 2) {
+      replay_map(std::atoll(argv[i]), std::atoll(argv[i + 1]));
+      ++cases;
+    }
+    std::printf("%d cases, %ld failures\n", cases, failures);
+    return failures ? 1 : 0;
+  }
   if (argc > 2 && std::string(argv[1]) == "--plant") {
     plant = std::string(argv[2]) == "tail" ? 1 : std::string(argv[2]) == "swizzle" ? 2 : 0;
     argv += 2;

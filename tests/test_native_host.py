@@ -5,7 +5,10 @@
   length and ragged tail, contiguous and (B, N, H, D)-strided layouts, and the
   2^24-element token-stride limit: every global read inside a valid row of the
   head, every LDS write and read inside its tile, the LDS fill a bijection
-  (tests/native/addr_replay.cpp). Two planted variants must fail it.
+  (tests/native/addr_replay.cpp). Two planted variants must fail it. The
+  same program checks the launch's workgroup -> (head, query block) mapping:
+  every item taken exactly once, rounds of consecutive items per XCD, XCD
+  loads within one chunk of each other; a planted mapping bug must fail it.
 - Sanitizer build: libsparge's host code (api.cpp, noalloc.hip) built with
   AddressSanitizer and UndefinedBehaviorSanitizer and driven through every
   rejection path and host helper (tests/native/abi_host_check.cpp).
@@ -55,6 +58,25 @@ def test_address_replay(replay):
 @pytest.mark.parametrize("plant", ["tail", "swizzle"])
 def test_address_replay_catches_planted_mistakes(replay, plant):
     rc, out = _run([replay, "--plant", plant, "64", "17776", "64", "128", "1000", "128"])
+    assert rc != 0 and "FAIL" in out
+
+
+# (items, round): every workload's B * H * ceil(N / 128) at D=128 (64
+# resident workgroups per XCD) and D=64 (128), plus small and boundary counts.
+MAP_CASES = [(2 * 8, 128), (12 * 256, 64), (60 * 139, 128), (40 * 591, 64), (24 * 931, 64),
+             (1, 64), (1, 128), (511, 64), (512, 64), (513, 64), (1023, 128), (1024, 128), (1025, 128),
+             (40 * 591, 128), (12 * 256, 128)]
+
+
+def test_workgroup_mapping(replay):
+    args = [str(x) for case in MAP_CASES for x in case]
+    rc, out = _run([replay, "--map"] + args)
+    assert rc == 0, out
+    assert f"{len(MAP_CASES)} cases, 0 failures" in out
+
+
+def test_workgroup_mapping_catches_planted_mistake(replay):
+    rc, out = _run([replay, "--map", "--plant", "deal", "3072", "64", "23640", "64"])
     assert rc != 0 and "FAIL" in out
 
 
