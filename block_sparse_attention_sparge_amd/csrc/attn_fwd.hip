@@ -77,10 +77,13 @@ constexpr int kBufferFlags = 0x00020000;
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedLdsRead = 0x100;
 
-// Resident workgroups per XCD (32 CUs): two per CU at D=128 (64 KB of LDS
-// each), four at D=64.
+// Consecutive work items dealt to an XCD at a time. At D=128 these are the
+// workgroups an XCD (32 CUs) holds at once, two per CU (64 KB of LDS each).
+// At D=64 an XCD holds 128, but its tiles are half the size and its L2 keeps
+// most of them anyway, and smaller chunks spread the last, partial round over
+// more XCDs: 32 measured best there.
 template <int D>
-constexpr int64_t kRound = D == 128 ? 64 : 128;
+constexpr int64_t kRound = D == 128 ? 64 : 32;
 static_assert(geom::kXcdCount == kNumXcd, "one XCD count");
 
 template <int D>
@@ -142,11 +145,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(Params p) {
   // Tile buffers: K stage 0, K stage 1, V stage 0, V stage 1.
   __shared__ __attribute__((aligned(1024))) char smem[4 * C::kTile];
 
-  // Workgroup -> (head, query block) by geom::work_item: the workgroups
-  // resident on an XCD (kRound of them) run in rounds that start, and walk
-  // their ascending lists, together, and each round takes consecutive query
-  // blocks (lists that overlap) of one head, while all XCDs work on about one
-  // head at a time. Causal lists grow with the block index, so each head's
+  // Workgroup -> (head, query block) by geom::work_item: at D=128 the
+  // workgroups resident on an XCD (kRound of them) run in rounds that start,
+  // and walk their ascending lists, together, and each round takes consecutive
+  // query blocks (lists that overlap) of one head, while all XCDs work on
+  // about one head at a time. Causal lists grow with the block index, so each head's
   // blocks are taken longest first: the short lists fill in at the end.
   int64_t bh, qb;
   {

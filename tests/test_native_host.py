@@ -61,11 +61,12 @@ def test_address_replay_catches_planted_mistakes(replay, plant):
     assert rc != 0 and "FAIL" in out
 
 
-# (items, round): every workload's B * H * ceil(N / 128) at D=128 (64
-# resident workgroups per XCD) and D=64 (128), plus small and boundary counts.
-MAP_CASES = [(2 * 8, 128), (12 * 256, 64), (60 * 139, 128), (40 * 591, 64), (24 * 931, 64),
-             (1, 64), (1, 128), (511, 64), (512, 64), (513, 64), (1023, 128), (1024, 128), (1025, 128),
-             (40 * 591, 128), (12 * 256, 128)]
+# (items, round): every workload's B * H * ceil(N / 128) with the chunk the
+# kernel uses for its head dimension (64 at D=128, 32 at D=64), other chunk
+# sizes, and small and boundary counts.
+MAP_CASES = [(2 * 8, 32), (12 * 256, 64), (60 * 139, 32), (40 * 591, 64), (24 * 931, 64),
+             (1, 64), (1, 32), (255, 32), (256, 32), (257, 32), (511, 64), (512, 64), (513, 64),
+             (60 * 139, 128), (40 * 591, 128)]
 
 
 def test_workgroup_mapping(replay):
