@@ -95,15 +95,25 @@ __host__ __device__ constexpr int v_read(int lane, int cc) {
 // order, so the `round` workgroups resident on an XCD at once run in rounds.
 // The items are cut into chunks of `round` and the chunks dealt round the XCDs,
 // 0..7 in even rounds and 7..0 in odd ones: each round on an XCD takes
-// consecutive items, and chunks of unequal work even out. Returns false for
-// the padding workgroups of the last round.
+// consecutive items, and chunks of unequal work even out. The items left for
+// a last, partial round are split over the XCDs in shares that differ by at
+// most one, so that no XCD runs a whole extra chunk while the others idle. Returns false for the padding
+// workgroups of the last round.
 constexpr int kXcdCount = 8;
 __host__ __device__ inline bool work_item(int64_t wid, int64_t n_items, int64_t round, int64_t& item) {
   const int64_t xcd = wid % kXcdCount;
   const int64_t it = wid / kXcdCount;
-  const int64_t r = it / round;
-  const int64_t chunk = r * kXcdCount + ((r & 1) ? kXcdCount - 1 - xcd : xcd);
-  item = chunk * round + (it - r * round);
+  const int64_t r = it / round, off = it - r * round;
+  const int64_t full = n_items / (round * kXcdCount);   // rounds with a whole chunk per XCD
+  if (r < full) {
+    item = (r * kXcdCount + ((r & 1) ? kXcdCount - 1 - xcd : xcd)) * round + off;
+  } else {
+    const int64_t rest = n_items - full * round * kXcdCount;
+    const int64_t per = rest / kXcdCount, extra = rest - per * kXcdCount;
+    const int64_t count = per + (xcd < extra ? 1 : 0);
+    const int64_t start = xcd * per + (xcd < extra ? xcd : extra);
+    item = off < count ? full * round * kXcdCount + start + off : n_items;
+  }
   return item < n_items;
 }
 // Workgroups of the launch: whole rounds of every XCD.
