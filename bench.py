@@ -36,7 +36,9 @@ PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector
 COPY_BYTES = 1 << 30         # calibration copy for the traffic counters
 METRIC = "block-sparse attn TFLOPS (effective + dense-equiv) & ms/call, N=75600 topk=0.3"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_wan14b-720p_topk0.3_traffic.json")
-ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_sparge_amd", "csrc", "attn_fwd.hip")
+# the attention kernel's sources: the traffic figure is used only while they are unchanged
+ATTN_SOURCES = [os.path.join(ROOT, "block_sparse_attention_sparge_amd", "csrc", f)
+                for f in ("attn_fwd.hip", "attn_geometry.h", "common.h")]
 
 
 def log(*a):
@@ -127,9 +129,12 @@ def kernel_durations_ms(fn, iters):
     return [a.elapsed_time(b) for a, b in evs]
 
 
-def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(workload: str):
@@ -140,7 +145,7 @@ def load_traffic(workload: str):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("attn_fwd_source_sha256_16") != source_hash(ATTN_SOURCE) or t.get("workload") != workload:
+    if t.get("attn_fwd_source_sha256_16") != source_hash(ATTN_SOURCES) or t.get("workload") != workload:
         return None
     return t.get("hbm_bytes_per_launch")
 
