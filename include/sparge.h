@@ -125,7 +125,8 @@ int sparge_pool_blocks(const uint16_t *x, int64_t B, int64_t H, int64_t N, int64
  *   mask_id  optional (NULL allowed): (B, H, N_QB, N_KB) uint8 contiguous, 1 for
  *            a kept block, 0 otherwise.
  *   kv_idx   (B, H, N_QB, k) int32 contiguous, k = sparge_topk_count(N_KB, topk):
- *            the kept key-block ids of each row in ascending order.
+ *            the kept key-block ids of each row in ascending order; entries
+ *            past the row's kv_cnt (causal rows keep fewer) are not written.
  *   kv_cnt   (B, H, N_QB) int32: the number kept in each row (k, or the
  *            row's causal count).
  * Ties in s go to the lower key-block index, so the result is deterministic.

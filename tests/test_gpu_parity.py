@@ -321,19 +321,23 @@ def test_plan_reuse_on_new_inputs(gpu_lib, parity_log):
     assert worst["max_abs"] <= 2e-2 and worst["mean_abs"] <= 2e-3
 
 
-def test_deterministic_full_size(gpu_lib):
+@pytest.mark.parametrize("causal", [False, True])
+def test_deterministic_full_size(gpu_lib, causal):
     """Bit-identical reruns at full occupancy (the Wan2.1-1.3B-shaped workload):
     masks, lists and outputs, through the one-call path and the list path."""
     wl = synth.WORKLOADS[1]
     dq, dk, dv = _dev(*synth.make_qkv(wl, seed=0))
-    o1, m1 = sp.attn_topk(dq, dk, dv, topk=0.5, return_mask=True)
-    o2, m2 = sp.attn_topk(dq, dk, dv, topk=0.5, return_mask=True)
-    _, i1, c1 = sp.predict_mask(sp.pool_blocks(dq, 128), sp.pool_blocks(dk, 64), wl.N, 0.5)
-    _, i2, c2 = sp.predict_mask(sp.pool_blocks(dq, 128), sp.pool_blocks(dk, 64), wl.N, 0.5)
-    a1 = sp.attn_from_list(dq, dk, dv, i1, c1)
-    a2 = sp.attn_from_list(dq, dk, dv, i2, c2)
+    o1, m1 = sp.attn_topk(dq, dk, dv, topk=0.5, return_mask=True, is_causal=causal)
+    o2, m2 = sp.attn_topk(dq, dk, dv, topk=0.5, return_mask=True, is_causal=causal)
+    _, i1, c1 = sp.predict_mask(sp.pool_blocks(dq, 128), sp.pool_blocks(dk, 64), wl.N, 0.5, is_causal=causal)
+    _, i2, c2 = sp.predict_mask(sp.pool_blocks(dq, 128), sp.pool_blocks(dk, 64), wl.N, 0.5, is_causal=causal)
+    a1 = sp.attn_from_list(dq, dk, dv, i1, c1, is_causal=causal)
+    a2 = sp.attn_from_list(dq, dk, dv, i2, c2, is_causal=causal)
     torch.cuda.synchronize()
-    assert torch.equal(m1, m2) and torch.equal(i1, i2) and torch.equal(c1, c2)
+    assert torch.equal(m1, m2) and torch.equal(c1, c2)
+    # list entries past a row's count are not written (causal rows keep fewer)
+    valid = torch.arange(i1.shape[-1], device=i1.device) < c1.unsqueeze(-1).long()
+    assert torch.equal(torch.where(valid, i1, 0), torch.where(valid, i2, 0))
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(a1.view(torch.int16), a2.view(torch.int16))
     assert torch.equal(a1.view(torch.int16), o1.view(torch.int16))
